@@ -1,0 +1,470 @@
+"""Plain numpy oracle (float64) of the streamed QKV-quant + packed-K/V attention path.
+
+TEST INFRASTRUCTURE: imported only by tests/, __graft_entry__.smoke() and the
+CPU-baseline leg of bench.py.  Shares no code with the HIP library.
+
+Page names used in citations:
+  [FR]  feature request "Streamed QKV Projection and Packed Low-Bit K/V Support for
+        Extreme Long-Sequence Attention" (comfy-kitchen issue and its mirror)
+  [VL]  "VRAM Lab" module page (ComfyUI-MAINodes vram_lab.py)
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "HEAD_DIM", "GROUP", "INT4", "INT8", "QMAX", "ROW_BYTES",
+    "hadamard_pm1", "rotation_matrix",
+    "f32_to_bf16_bits", "bf16_bits_to_f64", "f32_to_f16",
+    "chunk_ranges", "range_segments", "token_formats",
+    "project", "split_heads", "rms_norm", "rope_angles", "rope_split_half",
+    "rotate", "quantize_groups", "pack_int4", "unpack_int4", "pack_codes", "unpack_codes",
+    "dequantize", "qkv_quant_rows",
+    "packed_layout", "gather_packed_rows", "decode_head",
+    "softmax_attention", "online_merge", "attention_blockwise",
+    "attention_rotated_rows", "attention_model_rows", "attention_rows_from_store",
+    "working_set_bytes", "quality_vs_unquantised",
+]
+
+HEAD_DIM = 128          # head dimension of every workload ([VL] docstring: 7168 = 56 x 128)
+GROUP = 32              # quantisation group along head_dim (the workloads' "group 32")
+INT4 = 0                # token-range formats ([FR] "Mixed precision for conditioning")
+INT8 = 1
+QMAX = {INT4: 7, INT8: 127}
+ROW_BYTES = {INT4: HEAD_DIM // 2, INT8: HEAD_DIM}
+
+
+# --------------------------------------------------------------------------- rotation
+def hadamard_pm1(n: int = HEAD_DIM) -> np.ndarray:
+    """Sylvester Hadamard matrix with +-1 entries, n a power of two.
+
+    [VL] kvi8r section, `_hadamard`: start from the 1x1 matrix [1] and repeat the
+    2x2 block doubling [[h, h], [h, -h]] until the size reaches n.  (The page then
+    divides by sqrt(n); `rotation_matrix` does that.)"""
+    if n < 1 or n & (n - 1):
+        raise ValueError("n must be a power of two")
+    h = np.ones((1, 1), dtype=np.int64)
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def rotation_matrix(n: int = HEAD_DIM) -> np.ndarray:
+    """Orthonormal rotation H/sqrt(n) in float64 ([VL] kvi8r, `_hadamard`)."""
+    return hadamard_pm1(n).astype(np.float64) / math.sqrt(n)
+
+
+# --------------------------------------------------------------------------- rounding
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """fp32 -> bf16 bit pattern, round to nearest, ties to even (finite inputs)."""
+    u = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    return ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f32_to_f16(x) -> np.ndarray:
+    """fp32 -> fp16, IEEE round to nearest even (numpy's conversion)."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16)
+
+
+# --------------------------------------------------------------------------- chunk plan and range policy
+def chunk_ranges(n: int, size: int, min_tail: int = 512) -> List[Tuple[int, int]]:
+    """Row chunks of `size` rows; a last chunk shorter than `min_tail` is folded into
+    the one before it.  size <= 0 or size >= n gives one chunk.
+
+    [VL] helpers section, `_ranges`."""
+    if size <= 0 or size >= n:
+        return [(0, n)]
+    out = [(a, min(a + size, n)) for a in range(0, n, size)]
+    if len(out) > 1 and out[-1][1] - out[-1][0] < min_tail:
+        out.pop()
+        out[-1] = (out[-1][0], n)
+    return out
+
+
+def range_segments(n: int, ranges: Optional[Sequence[Tuple[int, int, int]]],
+                   boundary_multiple: int = 128) -> List[Tuple[int, int, int]]:
+    """Validate a token-range precision policy and return its segments.
+
+    [FR] "Mixed precision for conditioning": different K/V precision per token
+    range of the packed sequence (conditioning ranges at 8 bits, generated tokens
+    at rotated 4 bits).  [VL] segments are half-open (a, b) pairs in order.
+    Reading: the ranges must be sorted, contiguous, non-empty and cover [0, n);
+    every interior boundary is a multiple of `boundary_multiple` so that key tiles
+    never straddle two formats.  No ranges means one INT4 range."""
+    if not ranges:
+        return [(0, n, INT4)] if n > 0 else []
+    segs = []
+    pos = 0
+    for r in ranges:
+        b, e, f = int(r[0]), int(r[1]), int(r[2])
+        if f not in (INT4, INT8):
+            raise ValueError("unknown format %r" % f)
+        if b != pos:
+            raise ValueError("ranges must be contiguous from 0 (gap or overlap at %d)" % b)
+        if e <= b:
+            raise ValueError("empty or reversed range")
+        if e < n and e % boundary_multiple:
+            raise ValueError("interior boundary %d is not a multiple of %d" % (e, boundary_multiple))
+        segs.append((b, e, f))
+        pos = e
+    if pos != n:
+        raise ValueError("ranges end at %d, not at n=%d" % (pos, n))
+    return segs
+
+
+def token_formats(n: int, segments: Sequence[Tuple[int, int, int]]) -> np.ndarray:
+    fm = np.empty(n, dtype=np.int64)
+    for b, e, f in segments:
+        fm[b:e] = f
+    return fm
+
+
+# --------------------------------------------------------------------------- projection and per-head ops
+def project(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """y = x . W in float64 (bf16 products are exact in fp64; the sum is not rounded
+    to bf16, because the streamed projection never stores a bf16 QKV tensor:
+    [FR] "Proposed backend capability")."""
+    return bf16_bits_to_f64(x_bits) @ bf16_bits_to_f64(w_bits)
+
+
+def split_heads(y: np.ndarray, n_heads: int):
+    """Fused QKV columns are q | k | v, head h at columns [128h, 128h+128) of each
+    ([VL] block section, `_phase1_kv`: split of the fused projection into three
+    equal parts, each viewed as heads x 128)."""
+    d = n_heads * HEAD_DIM
+    assert y.shape[-1] == 3 * d
+    r = y.shape[0]
+    return (y[:, :d].reshape(r, n_heads, HEAD_DIM),
+            y[:, d:2 * d].reshape(r, n_heads, HEAD_DIM),
+            y[:, 2 * d:].reshape(r, n_heads, HEAD_DIM))
+
+
+def rms_norm(u: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """Per-head RMSNorm over the last (head_dim) axis: u / sqrt(mean(u^2) + eps) * w.
+    [VL] helpers section, `_norm_rope` (q_norm / k_norm before RoPE)."""
+    u = np.asarray(u, dtype=np.float64)
+    ms = np.mean(u * u, axis=-1, keepdims=True)
+    return u / np.sqrt(ms + eps) * np.asarray(w, dtype=np.float64)
+
+
+def rope_angles(positions: np.ndarray, theta: float = 10000.0, rot_dim: int = HEAD_DIM):
+    """cos/sin of pos * theta^(-2i/rot_dim), i < rot_dim/2, in float64 [R, rot_dim/2].
+    The workloads name a 1D RoPE with theta 10000 over token positions."""
+    half = rot_dim // 2
+    i = np.arange(half, dtype=np.float64)
+    inv = theta ** (-2.0 * i / rot_dim)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def rope_split_half(u: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """Split-half RoPE ([VL] helpers, `_norm_rope`: "split-half" rotation over
+    rot_dim = 2 x table width): pairs (i, i + 64) rotate by the angle of row i:
+    (a, b) -> (a cos - b sin, b cos + a sin).  u is [R, H, 128]; cos/sin [R, 64]."""
+    half = cos.shape[-1]
+    a = u[..., :half]
+    b = u[..., half:2 * half]
+    c = cos[:, None, :]
+    s = sin[:, None, :]
+    out = np.array(u, dtype=np.float64, copy=True)
+    out[..., :half] = a * c - b * s
+    out[..., half:2 * half] = b * c + a * s
+    return out
+
+
+def rotate(u: np.ndarray) -> np.ndarray:
+    """r = u . H / sqrt(128) per 128-vector, computed in float64 and rounded once to
+    fp32.  [FR] "Quality-oriented low-bit format" (orthogonal / Hadamard-style
+    rotation before quantising); [VL] kvi8r `_Int8KV.store` (rotate by the
+    orthonormal Hadamard along the head dim).  Reading: no bf16/fp16 rounding
+    between the fp32 accumulator and the quantiser."""
+    H = hadamard_pm1(HEAD_DIM).astype(np.float64)
+    return ((np.asarray(u, dtype=np.float64) @ H) / math.sqrt(HEAD_DIM)).astype(np.float32)
+
+
+# --------------------------------------------------------------------------- quantise / pack
+def quantize_groups(r: np.ndarray, qmax: int):
+    """Group quantisation of fp32 rotated vectors [..., 128] in groups of 32.
+
+    For each group: a = max |r| (fp32); s = fp16_RNE(a / qmax) with the division
+    in IEEE fp32; if s == 0 every code is 0; otherwise c = clamp(rne(r / fp32(s)),
+    -qmax, qmax) with round-half-to-even and IEEE fp32 division.
+    [VL] precision-probe section, `_fq_int4` (absmax / 7, round, clamp) and kvi8r
+    `_Int8KV.store` (absmax / 127, round, clamp to +-127); the workloads give
+    group 32 along head_dim and fp16 scales.  Returns (codes int8, scales fp16)."""
+    r = np.ascontiguousarray(np.asarray(r, dtype=np.float32))
+    lead = r.shape[:-1]
+    g = r.reshape(lead + (HEAD_DIM // GROUP, GROUP))
+    a = np.max(np.abs(g), axis=-1)                                  # fp32, exact
+    s16 = (a / np.float32(qmax)).astype(np.float32).astype(np.float16)
+    s32 = s16.astype(np.float32)
+    safe = np.where(s32 == 0, np.float32(1), s32)
+    q = np.rint(g / safe[..., None])                                # fp32 division, RNE
+    q = np.clip(q, -qmax, qmax)
+    q = np.where((s32 == 0)[..., None], 0, q)
+    return q.astype(np.int8).reshape(r.shape), s16
+
+
+def pack_int4(codes: np.ndarray) -> np.ndarray:
+    """Two's-complement nibbles, code 2i in bits 0-3 and code 2i+1 in bits 4-7."""
+    c = np.asarray(codes, dtype=np.int64) & 0xF
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_int4(packed: np.ndarray) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.int64)
+    lo = p & 0xF
+    hi = (p >> 4) & 0xF
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def pack_codes(codes: np.ndarray, fmt: int) -> np.ndarray:
+    if fmt == INT4:
+        return pack_int4(codes)
+    return np.asarray(codes, dtype=np.int8).view(np.uint8)
+
+
+def unpack_codes(packed: np.ndarray, fmt: int) -> np.ndarray:
+    if fmt == INT4:
+        return unpack_int4(packed)
+    return np.asarray(packed, dtype=np.uint8).view(np.int8)
+
+
+def dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """k_r = code * scale per group, exact in float64 (rotated basis)."""
+    c = np.asarray(codes, dtype=np.float64)
+    s = np.asarray(scales, dtype=np.float16).astype(np.float64)
+    lead = c.shape[:-1]
+    return (c.reshape(lead + (HEAD_DIM // GROUP, GROUP)) * s[..., None]).reshape(c.shape)
+
+
+# --------------------------------------------------------------------------- the streamed QKV-quant step for chosen rows
+def qkv_quant_rows(x_bits_rows: np.ndarray, w_bits: np.ndarray, n_heads: int,
+                   positions: np.ndarray, fmts: np.ndarray,
+                   q_norm_w: Optional[np.ndarray] = None, k_norm_w: Optional[np.ndarray] = None,
+                   eps: float = 1e-6, rope_theta: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """What the streamed QKV-quant computes for the given token rows.
+
+    [FR] "Proposed backend capability": hidden states go through a tiled QKV
+    projection; Q is kept in bf16; K and V are rotated, quantised and packed.
+    [VL] block section, `_phase1_kv`: projection -> split -> (RMSNorm + RoPE of q
+    and k) -> store.  Row r uses token position positions[r] for RoPE and format
+    fmts[r] (INT4 or INT8) for its K/V codes.
+
+    Returns q_bits [R, d] uint16 (bf16, model basis), k_codes / v_codes
+    [R, H, 128] int8, k_scales / v_scales [R, H, 4] fp16."""
+    y = project(x_bits_rows, w_bits)
+    q, k, v = split_heads(y, n_heads)
+    if q_norm_w is not None:
+        q = rms_norm(q, q_norm_w, eps)
+        k = rms_norm(k, k_norm_w, eps)
+    if rope_theta is not None:
+        cos, sin = rope_angles(positions, rope_theta)
+        q = rope_split_half(q, cos, sin)
+        k = rope_split_half(k, cos, sin)
+    r_rows = q.shape[0]
+    q_bits = f32_to_bf16_bits(q.astype(np.float32)).reshape(r_rows, n_heads * HEAD_DIM)
+    kr = rotate(k)
+    vr = rotate(v)
+    out = {"q_bits": q_bits}
+    for name, rr in (("k", kr), ("v", vr)):
+        codes = np.zeros(rr.shape, dtype=np.int8)
+        scales = np.zeros(rr.shape[:-1] + (HEAD_DIM // GROUP,), dtype=np.float16)
+        for f in (INT4, INT8):
+            sel = np.asarray(fmts) == f
+            if np.any(sel):
+                c, s = quantize_groups(rr[sel], QMAX[f])
+                codes[sel] = c
+                scales[sel] = s
+        out[name + "_codes"] = codes
+        out[name + "_scales"] = scales
+    out["k_rot_f32"] = kr
+    out["v_rot_f32"] = vr
+    return out
+
+
+# --------------------------------------------------------------------------- packed store layout
+def packed_layout(n: int, n_heads: int, segments: Sequence[Tuple[int, int, int]]):
+    """Byte layout of a packed K (or V) store.
+
+    Reading of [FR] "Proposed backend capability" / "Quality-oriented low-bit
+    format" (fixed-width packed tiles a kernel can address directly) and of [VL]
+    kvi8r (head-major [heads, tokens, head_dim] store): each segment [b, e) of
+    format f holds its codes head-major, row (h, t) at
+    offset_s + (h * (e - b) + (t - b)) * row_bytes(f); segments follow each other.
+    Scales are separate, fp16 [H, N, 4] over the whole sequence."""
+    out = []
+    off = 0
+    for b, e, f in segments:
+        out.append({"begin": b, "end": e, "fmt": f, "offset": off, "row_bytes": ROW_BYTES[f]})
+        off += n_heads * (e - b) * ROW_BYTES[f]
+    return out, off
+
+
+def gather_packed_rows(packed: np.ndarray, scales: np.ndarray, layout, n_heads: int,
+                       rows: np.ndarray):
+    """Codes [R, H, 128] int8 and scales [R, H, 4] fp16 of the given token rows."""
+    packed = np.asarray(packed, dtype=np.uint8).reshape(-1)
+    sc = np.asarray(scales).reshape(n_heads, -1, HEAD_DIM // GROUP)
+    rows = np.asarray(rows, dtype=np.int64)
+    codes = np.zeros((rows.size, n_heads, HEAD_DIM), dtype=np.int8)
+    for seg in layout:
+        sel = np.nonzero((rows >= seg["begin"]) & (rows < seg["end"]))[0]
+        if sel.size == 0:
+            continue
+        rb = seg["row_bytes"]
+        L = seg["end"] - seg["begin"]
+        for h in range(n_heads):
+            start = seg["offset"] + (h * L + (rows[sel] - seg["begin"])) * rb
+            idx = start[:, None] + np.arange(rb)[None, :]
+            codes[sel, h] = unpack_codes(packed[idx], seg["fmt"])
+    return codes, np.ascontiguousarray(sc[:, rows, :].transpose(1, 0, 2))
+
+
+def decode_head(packed: np.ndarray, scales: np.ndarray, layout, n_heads: int, head: int,
+                begin: int, end: int) -> np.ndarray:
+    """Dequantised rotated-basis vectors of one head for tokens [begin, end), float64."""
+    packed = np.asarray(packed, dtype=np.uint8).reshape(-1)
+    sc = np.asarray(scales).reshape(n_heads, -1, HEAD_DIM // GROUP)
+    out = np.empty((end - begin, HEAD_DIM), dtype=np.float64)
+    for seg in layout:
+        lo, hi = max(begin, seg["begin"]), min(end, seg["end"])
+        if lo >= hi:
+            continue
+        rb = seg["row_bytes"]
+        L = seg["end"] - seg["begin"]
+        start = seg["offset"] + (head * L + (lo - seg["begin"])) * rb
+        blob = packed[start:start + (hi - lo) * rb].reshape(hi - lo, rb)
+        out[lo - begin:hi - begin] = dequantize(unpack_codes(blob, seg["fmt"]), sc[head, lo:hi])
+    return out
+
+
+# --------------------------------------------------------------------------- attention
+def softmax_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
+    """Exact single-pass softmax attention in float64 for one head.
+
+    q [R, D], k [S, D], v [S, D] -> o [R, D], lse [R] (natural log).  Scores
+    s = scale * q.k; the row maximum is subtracted before exp; lse = m + ln sum e^(s-m).
+    Non-causal, no mask ([VL] helpers, `_blockwise_attention`: flash call without
+    mask or causality; softmax scale head_dim^-1/2)."""
+    s = (np.asarray(q, np.float64) @ np.asarray(k, np.float64).T) * scale
+    m = np.max(s, axis=-1, keepdims=True)
+    p = np.exp(s - m)
+    l = np.sum(p, axis=-1, keepdims=True)
+    o = (p @ np.asarray(v, np.float64)) / l
+    return o, (m + np.log(l))[:, 0]
+
+
+def online_merge(o_acc, lse_acc, o, lse):
+    """Online-softmax merge of a partial (o, lse) into (o_acc, lse_acc).
+
+    [VL] kvi8r section, `_online_combine`: lse' = logaddexp(lse_acc, lse);
+    o' = o_acc * exp(lse_acc - lse') + o * exp(lse - lse').  A None accumulator
+    takes the partial as is."""
+    if o_acc is None:
+        return np.array(o, dtype=np.float64, copy=True), np.array(lse, dtype=np.float64, copy=True)
+    new = np.logaddexp(lse_acc, lse)
+    return (o_acc * np.exp(lse_acc - new)[:, None] + o * np.exp(lse - new)[:, None]), new
+
+
+def attention_blockwise(q, k, v, scale, block: int, min_tail: int = 512):
+    """Attention over K/V blocks `chunk_ranges(S, block, min_tail)` merged with
+    `online_merge` ([VL] helpers, `_blockwise_attention`; kvi8r
+    `_blockwise_attention_q`)."""
+    o_acc = lse_acc = None
+    for a, b in chunk_ranges(k.shape[0], block, min_tail):
+        o, lse = softmax_attention(q, k[a:b], v[a:b], scale)
+        o_acc, lse_acc = online_merge(o_acc, lse_acc, o, lse)
+    return o_acc, lse_acc
+
+
+def attention_rotated_rows(q_bits_head: np.ndarray, k_rot: np.ndarray, v_rot: np.ndarray,
+                           scale: float, kv_block: int = 0):
+    """Attention of bf16 query rows (model basis) against dequantised K/V kept in
+    the rotated basis.
+
+    [VL] kvi8r `_Int8KV` docstring and `_blockwise_attention_q`: since H/sqrt(n)
+    is orthogonal, q.k = (qH).(kH) and P.V = (P.(VH)).H^T; so the queries are
+    rotated once, attention runs against the rotated store, and the output is
+    rotated back once (H is symmetric, so H^T = H).  kv_block > 0 merges KV blocks
+    by log-sum-exp.  Returns o [R, 128] (model basis) and lse [R]."""
+    R = rotation_matrix(HEAD_DIM)
+    qr = bf16_bits_to_f64(q_bits_head) @ R
+    if kv_block and kv_block > 0:
+        o_r, lse = attention_blockwise(qr, k_rot, v_rot, scale, kv_block)
+    else:
+        o_r, lse = softmax_attention(qr, k_rot, v_rot, scale)
+    return o_r @ R.T, lse
+
+
+def attention_model_rows(q_bits_head: np.ndarray, k_rot: np.ndarray, v_rot: np.ndarray,
+                         scale: float):
+    """The same attention in the model basis: the dequantised K and V are rotated
+    back first (k = k_r . (H/sqrt(128))^T) and the queries are used as stored."""
+    R = rotation_matrix(HEAD_DIM)
+    return softmax_attention(bf16_bits_to_f64(q_bits_head), k_rot @ R.T, v_rot @ R.T, scale)
+
+
+def attention_rows_from_store(q_bits: np.ndarray, rows: np.ndarray, kpack, vpack, kscale,
+                              vscale, layout, n_heads: int, n_tokens: int,
+                              scale: Optional[float] = None, kv_block: int = 0,
+                              kv_begin: int = 0, kv_end: Optional[int] = None,
+                              heads: Optional[Sequence[int]] = None):
+    """Packed-K/V attention for the query rows `rows` against keys [kv_begin, kv_end).
+
+    q_bits is [R, d] bf16 bits of those rows (model basis).  [FR] "Dense fallback
+    is important": keys are decoded from the packed store (here: head by head, in
+    float64), never from a bf16 K/V.  Returns o [R, d] and lse [H, R]."""
+    if scale is None:
+        scale = HEAD_DIM ** -0.5
+    if kv_end is None:
+        kv_end = n_tokens
+    heads = range(n_heads) if heads is None else heads
+    Rn = len(rows)
+    o = np.zeros((Rn, n_heads * HEAD_DIM), dtype=np.float64)
+    lse = np.zeros((n_heads, Rn), dtype=np.float64)
+    for h in heads:
+        kr = decode_head(kpack, kscale, layout, n_heads, h, kv_begin, kv_end)
+        vr = decode_head(vpack, vscale, layout, n_heads, h, kv_begin, kv_end)
+        qh = q_bits[:, h * HEAD_DIM:(h + 1) * HEAD_DIM]
+        oh, lh = attention_rotated_rows(qh, kr, vr, scale, kv_block)
+        o[:, h * HEAD_DIM:(h + 1) * HEAD_DIM] = oh
+        lse[h] = lh
+    return o, lse
+
+
+# --------------------------------------------------------------------------- memory
+def working_set_bytes(n: int, d_model: int, segments: Sequence[Tuple[int, int, int]]):
+    """Closed-form bytes of the fused bf16 QKV versus Q bf16 + packed K/V + scales.
+    [FR] "Potential reduction": Q kept at bf16, K and V at 4 bits, plus metadata."""
+    H = d_model // HEAD_DIM
+    codes = sum((e - b) * H * ROW_BYTES[f] for b, e, f in segments)
+    scales = n * H * (HEAD_DIM // GROUP) * 2
+    q = 2 * n * d_model
+    return {"bf16_qkv": 6 * n * d_model, "q": q, "k_codes": codes, "v_codes": codes,
+            "k_scales": scales, "v_scales": scales,
+            "packed_total": q + 2 * codes + 2 * scales}
+
+
+def quality_vs_unquantised(q_bits_head, k_model, v_model, k_rot_hat, v_rot_hat):
+    """Relative L2 error of attention over dequantised K/V against the same
+    attention over the unquantised K/V (information only; parity unpinned: the
+    pages give no value for this format on these inputs)."""
+    scale = HEAD_DIM ** -0.5
+    o_ref, _ = softmax_attention(bf16_bits_to_f64(q_bits_head), k_model, v_model, scale)
+    o_q, _ = attention_rotated_rows(q_bits_head, k_rot_hat, v_rot_hat, scale)
+    return float(np.linalg.norm(o_q - o_ref) / max(np.linalg.norm(o_ref), 1e-300))
