@@ -1,0 +1,249 @@
+"""Benchmark of the streamed QKV-quant + packed-K/V attention hot path on one GPU.
+
+One step = the whole path over one batch of synthetic input already resident in
+HBM: streamed_qkv_quant over all row chunks (projection, RMSNorm/RoPE where the
+workload has them, Hadamard rotation, quantisation, packing), then
+packed_kv_attention over all KV blocks (log-sum-exp merge where the workload
+blocks the keys).  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "packed-KV attention TFLOP/s + streamed QKV-quant tokens/s; peak HBM bytes"
+PEAK_TFLOPS_F16 = 2500.0   # MI355X dense bf16 / f16 MFMA (published)
+DEFAULT_WORKLOAD = "h3_217k_normrope"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=4, help="heads in the oracle's attention sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import streamed_qkv_gemm_amd as sqg
+    import synth
+
+    sqg.load()
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU: the library has no CPU path")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.WORKLOADS[args.workload]
+    N, d, H = wl.n_tokens, wl.d_model, wl.n_heads
+    print("[bench] workload %s N=%d d=%d steps=%d warmup=%d" % (wl.name, N, d, args.steps, args.warmup),
+          file=sys.stderr, flush=True)
+
+    # ---- inputs resident in HBM
+    x = synth.make_x(N, d, wl.outlier_frac, seed=wl.seed_base + 1, device=dev,
+                     outlier_seed=wl.seed_base + 3)
+    w = synth.make_w(d, seed=wl.seed_base + 2, device=dev)
+    kw = {}
+    norm = None
+    if wl.norm_rope:
+        norm = synth.make_norm_weights(wl.seed_base + 4)
+        kw["q_norm_w"], kw["k_norm_w"] = norm[0].to(dev), norm[1].to(dev)
+        kw["rope_cos"], kw["rope_sin"] = sqg.rope_table(N, 10000.0, device=dev)
+    torch.cuda.synchronize()
+    input_bytes = torch.cuda.memory_allocated(dev)
+
+    store = sqg.alloc_store(N, d, wl.ranges, device=dev)
+    o = torch.empty((N, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((H, N), dtype=torch.float32, device=dev)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        sqg.streamed_qkv_quant(x, w, ranges=wl.ranges, chunk_rows=wl.chunk_rows, out=store, **kw)
+        if ev:
+            ev[1].record(stream)
+        sqg.packed_kv_attention(store, kv_block=wl.kv_block, o=o, lse=lse)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    peak_alloc = torch.cuda.max_memory_allocated(dev)
+    qkv_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    att_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    step_ms = sum(e[0].elapsed_time(e[2]) for e in evs) / args.steps
+
+    qkv_flop = 2.0 * N * d * 3 * d
+    att_flop = 4.0 * N * N * H * 128
+    n_chunks = len(sqg.chunk_ranges(N, wl.chunk_rows, 512))
+    n_att_launch = len(sqg.chunk_ranges(N, wl.kv_block, 512))
+    L = store["layout"]
+    packed_ws = L["q_bytes"] + 2 * L["pack_bytes"] + 2 * L["scale_bytes"]
+    att_tflops = att_flop / (att_ms * 1e-3) / 1e12
+    qkv_tflops = qkv_flop / (qkv_ms * 1e-3) / 1e12
+
+    # ---- bf16-materialising baseline: x @ W into a bf16 [N, 3d] tensor (library GEMM)
+    bf16_base = None
+    if not args.no_bf16_baseline:
+        del_ok = True
+        try:
+            torch.cuda.synchronize()
+            torch.cuda.reset_peak_memory_stats(dev)
+            base0 = torch.cuda.memory_allocated(dev)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            y = torch.matmul(x, w)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            y = torch.matmul(x, w)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            bf16_base = {"extra_peak_bytes": torch.cuda.max_memory_allocated(dev) - base0,
+                         "qkv_bytes": y.numel() * 2, "gemm_ms": e0.elapsed_time(e1)}
+            del y
+        except RuntimeError as exc:  # pragma: no cover - reported, not fatal
+            del_ok = False
+            bf16_base = {"error": str(exc)[:200]}
+        torch.cuda.empty_cache()
+
+    result = {
+        "metric": METRIC,
+        "value": (qkv_flop + att_flop) / (step_ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 projection, f16 attention, int4/int8 K/V",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "n_tokens": N, "d_model": d, "n_heads": H, "head_dim": 128,
+                   "ranges": wl.range_list(), "chunk_rows": wl.chunk_rows, "kv_block": wl.kv_block,
+                   "norm_rope": wl.norm_rope, "kv_format": "Hadamard-rotated INT4/INT8, group 32, fp16 scales",
+                   "parallelism": "none (1 GPU)"},
+        "attention_tflops": att_tflops,
+        "attention_ms": att_ms,
+        "qkv_quant_tokens_per_s": N / (qkv_ms * 1e-3),
+        "qkv_quant_tflops": qkv_tflops,
+        "qkv_quant_ms": qkv_ms,
+        "qkv_quant_mfma_frac": qkv_tflops / PEAK_TFLOPS_F16,
+        "peak_alloc_bytes": peak_alloc,
+        "input_bytes": input_bytes,
+        "qkv_working_set_bytes": packed_ws,
+        "bf16_qkv_bytes": L["bf16_qkv_bytes"],
+        "working_set_ratio": packed_ws / L["bf16_qkv_bytes"],
+        "bf16_materialising_baseline": bf16_base,
+        "wall_s_timed": wall,
+        "roofline": {
+            "kernel": "packed_attention_kernel",
+            "bound": "mfma",
+            "achieved": att_tflops,
+            "peak": PEAK_TFLOPS_F16,
+            "unit": "TFLOP/s",
+            "frac": att_tflops / PEAK_TFLOPS_F16,
+            "traffic": None,
+            "launches_per_step": n_att_launch,
+            "avg_launch_ms": att_ms / n_att_launch,
+            "algorithmic_flop_per_step": att_flop,
+        },
+        "qkv_roofline": {
+            "kernel": "qkv_quant_kernel", "bound": "mfma", "achieved": qkv_tflops,
+            "peak": PEAK_TFLOPS_F16, "unit": "TFLOP/s", "frac": qkv_tflops / PEAK_TFLOPS_F16,
+            "launches_per_step": n_chunks, "avg_launch_ms": qkv_ms / n_chunks,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, x, w, norm, store, args.cpu_heads)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, x, w, norm, store, n_heads_sample):
+    """The oracle as it stands, timed on this host's cores on a bounded sample:
+    64 token rows of the QKV-quant and 8 query rows x `n_heads_sample` heads x all
+    keys of the attention.  Reported in the same unit as the GPU figure."""
+    import numpy as np
+    import threadpoolctl
+    import torch
+
+    import oracle
+    import synth
+
+    N, d, H = wl.n_tokens, wl.d_model, wl.n_heads
+    dev = x.device
+    extra = [b for (b, _, _) in wl.range_list()[1:]]
+    rows = synth.sample_rows(N, 64, seed=wl.seed_base + 5,
+                             must=synth.boundary_rows(N, wl.chunk_rows, extra)[:32]).numpy()
+    xb = synth.bf16_bits(x[torch.from_numpy(rows).to(dev)])
+    wb = synth.bf16_bits(w)
+    segs = oracle.range_segments(N, wl.ranges)
+    fm = oracle.token_formats(N, segs)[rows]
+    okw = {}
+    if wl.norm_rope:
+        okw = dict(q_norm_w=norm[0].numpy(), k_norm_w=norm[1].numpy(), eps=1e-6, rope_theta=10000.0)
+    threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    t0 = time.perf_counter()
+    oracle.qkv_quant_rows(xb, wb, H, rows, fm, **okw)
+    t_qkv = time.perf_counter() - t0
+
+    layout, _ = oracle.packed_layout(N, H, segs)
+    kp, vp = store["kpack"].cpu().numpy(), store["vpack"].cpu().numpy()
+    ks, vs = store["kscale"].cpu().numpy(), store["vscale"].cpu().numpy()
+    qrows = synth.sample_rows(N, 8, seed=wl.seed_base + 6).numpy()
+    qb = synth.bf16_bits(store["q"])[qrows]
+    heads = list(range(0, H, max(1, H // n_heads_sample)))[:n_heads_sample]
+    t0 = time.perf_counter()
+    oracle.attention_rows_from_store(qb, qrows, kp, vp, ks, vs, layout, H, N, kv_block=wl.kv_block,
+                                     heads=heads)
+    t_att = time.perf_counter() - t0
+    qkv_flop = 2.0 * len(rows) * d * 3 * d
+    att_flop = 4.0 * len(qrows) * N * len(heads) * 128
+    return {
+        "value": (qkv_flop + att_flop) / (t_qkv + t_att) / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": "QKV-quant of %d token rows (%.2f s, %.1f tokens/s) + attention of %d query rows x "
+                  "%d heads x all %d keys decoded from the GPU's packed store (%.2f s)"
+                  % (len(rows), t_qkv, len(rows) / t_qkv, len(qrows), len(heads), N, t_att),
+        "qkv_tokens_per_s": len(rows) / t_qkv,
+        "attention_tflops": att_flop / t_att / 1e12,
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+if __name__ == "__main__":
+    main()

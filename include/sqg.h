@@ -1,0 +1,220 @@
+/*
+ * sqg.h -- C ABI of libsqg.so: streamed QKV-quant and packed-K/V attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes comes from two pages:
+ *   [FR] feature request "Streamed QKV Projection and Packed Low-Bit K/V Support
+ *        for Extreme Long-Sequence Attention" (comfy-kitchen issue and mirror);
+ *   [VL] "VRAM Lab" module page (ComfyUI-MAINodes vram_lab.py).
+ *
+ * Conventions shared by every call
+ *   - Pointers marked "device" are HIP device pointers; "host" pointers are read
+ *     during the call only.  The caller owns every buffer.  The library never
+ *     allocates or frees device memory, keeps no pointer after returning, never
+ *     synchronises the stream, and holds no mutable global state except a
+ *     thread-local error message.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work is
+ *     enqueued on it and the call returns without waiting.
+ *   - Device pointers must be 16-byte aligned and row strides (in elements) must be
+ *     multiples of 8, so that every tile is moved with 128-bit accesses.
+ *   - Every argument is checked on the host before the first launch: a call that
+ *     returns an error has enqueued nothing.  sqg_last_error() then describes it.
+ *   - head_dim is 128 and the quantisation group is 32 values along head_dim.
+ */
+#ifndef SQG_H
+#define SQG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(SQG_BUILDING_LIBRARY)
+#define SQG_API __attribute__((visibility("default")))
+#else
+#define SQG_API
+#endif
+
+#define SQG_VERSION 100          /* 1.0.0 */
+#define SQG_HEAD_DIM 128
+#define SQG_GROUP 32
+#define SQG_MAX_SEGMENTS 16
+
+typedef enum sqg_status {
+  SQG_OK = 0,
+  SQG_ERR_INVALID_ARGUMENT = -1,   /* null pointer, bad size, bad range policy ... */
+  SQG_ERR_UNSUPPORTED = -2,        /* shape outside what the kernels implement */
+  SQG_ERR_MISALIGNED = -3,         /* pointer not 16-byte aligned or stride not a multiple of 8 */
+  SQG_ERR_HIP = -5                 /* a HIP launch reported an error */
+} sqg_status;
+
+/* K/V storage format of a token range.  [FR] "Quality-oriented low-bit format"
+ * (fixed-width rotated INT4 with per-group scales) and "Mixed precision for
+ * conditioning" (8-bit K/V for conditioning ranges).  Both formats hold codes of
+ * the Hadamard-rotated vector with one fp16 scale per group of 32 values. */
+typedef enum sqg_kv_format {
+  SQG_INT4_ROT = 0,   /* codes in [-7, 7], two per byte, code 2i in bits 0-3 */
+  SQG_INT8_ROT = 1    /* codes in [-127, 127], one per byte (two's complement) */
+} sqg_kv_format;
+
+typedef enum sqg_out_dtype { SQG_F32 = 0, SQG_BF16 = 1, SQG_F16 = 2 } sqg_out_dtype;
+
+/* One token range [begin, end) of the precision policy. */
+typedef struct sqg_range {
+  int64_t begin;
+  int64_t end;
+  int32_t fmt;        /* sqg_kv_format */
+  int32_t reserved;   /* must be 0 */
+} sqg_range;
+
+/* Byte layout of the packed K (and, identically, V) store, filled by sqg_kv_layout.
+ * Segment s covers tokens [seg_begin[s], seg_end[s]) in format seg_fmt[s]; the
+ * codes of (head h, token t) start at byte
+ *   seg_offset[s] + (h * (seg_end[s] - seg_begin[s]) + (t - seg_begin[s])) * seg_row_bytes[s]
+ * of the kpack (vpack) buffer, where seg_row_bytes is 64 for INT4 and 128 for INT8.
+ * Scales are fp16 [n_heads, n_tokens, 4]: group g of (h, t) at element (h*N + t)*4 + g. */
+typedef struct sqg_layout {
+  int64_t n_tokens;
+  int32_t n_heads;
+  int32_t n_segments;
+  int64_t seg_begin[SQG_MAX_SEGMENTS];
+  int64_t seg_end[SQG_MAX_SEGMENTS];
+  int64_t seg_offset[SQG_MAX_SEGMENTS];
+  int32_t seg_fmt[SQG_MAX_SEGMENTS];
+  int32_t seg_row_bytes[SQG_MAX_SEGMENTS];
+  int64_t q_bytes;        /* bf16 Q [N, d] */
+  int64_t pack_bytes;     /* bytes of kpack, and of vpack */
+  int64_t scale_bytes;    /* bytes of kscale, and of vscale */
+  int64_t bf16_qkv_bytes; /* the fused bf16 [N, 3d] tensor this layout replaces */
+} sqg_layout;
+
+/* Arguments of sqg_streamed_qkv_quant. */
+typedef struct sqg_qkv_args {
+  int64_t n_tokens;            /* N >= 0 (0 is a no-op) */
+  int32_t d_model;             /* d = 128 * n_heads, a multiple of 256 */
+  int32_t n_heads;
+  const void* x;               /* device, bf16 [N, ldx] row-major */
+  int64_t ldx;
+  const void* w_qkv;           /* device, bf16 [d, 3d] row-major: columns q | k | v, head h at 128h */
+  int64_t ldw;                 /* >= 3d */
+  const float* q_norm_w;       /* device, fp32 [128] or NULL: per-head RMSNorm gain of q */
+  const float* k_norm_w;       /* device, fp32 [128] or NULL (both or neither) */
+  float eps;                   /* RMSNorm epsilon */
+  const float* rope_cos;       /* device, fp32 [N, 64] or NULL (both or neither); see sqg_rope_table */
+  const float* rope_sin;
+  const sqg_range* ranges;     /* host; NULL with n_ranges 0 = all INT4 */
+  int32_t n_ranges;
+  int32_t reserved;
+  int64_t chunk_rows;          /* rows per launch (multiple of 128); 0 = one launch */
+  int64_t min_tail;            /* a last chunk shorter than this joins the previous one; <0 = 512 */
+  void* q;                     /* device, bf16 [N, ldq] out (model basis) */
+  int64_t ldq;
+  void* kpack;                 /* device, layout.pack_bytes out */
+  void* vpack;
+  void* kscale;                /* device, fp16 [H, N, 4] out */
+  void* vscale;
+} sqg_qkv_args;
+
+/* Arguments of sqg_packed_kv_attention. */
+typedef struct sqg_attn_args {
+  int64_t n_tokens;            /* N: rows of Q and keys in the store */
+  int32_t d_model;
+  int32_t n_heads;
+  const void* q;               /* device, bf16 [N, ldq] (model basis) */
+  int64_t ldq;
+  const void* kpack;           /* device, as written by sqg_streamed_qkv_quant */
+  const void* vpack;
+  const void* kscale;          /* device, fp16 [H, N, 4] */
+  const void* vscale;
+  const sqg_range* ranges;     /* host: the policy the store was written with */
+  int32_t n_ranges;
+  int32_t o_dtype;             /* sqg_out_dtype */
+  int64_t q_begin, q_end;      /* query rows [q_begin, q_end); q_end 0 = N */
+  int64_t kv_begin, kv_end;    /* keys [kv_begin, kv_end); kv_end 0 = N; kv_begin % 128 == 0 */
+  int64_t kv_block;            /* 0 = one pass; > 0 = key blocks of this many keys (multiple of
+                                  128, last block shorter than 512 folded) merged by log-sum-exp */
+  int32_t accumulate;          /* 1 = merge into the existing (O, lse) instead of overwriting */
+  float softmax_scale;         /* 0 = 1/sqrt(128) */
+  void* o;                     /* device, [N, ldo] of o_dtype, out (model basis) */
+  int64_t ldo;
+  float* lse;                  /* device, fp32 [H, N] natural-log LSE out, or NULL;
+                                  required when accumulate or kv_block > 0 */
+} sqg_attn_args;
+
+/* Library version (SQG_VERSION of the build). */
+SQG_API int sqg_version(void);
+
+/* Fixed text for a status code. */
+SQG_API const char* sqg_status_string(int status);
+
+/* Detail of the last error on the calling thread ("" after a successful call). */
+SQG_API const char* sqg_last_error(void);
+
+/* sizeof of the argument structs, so bindings can check their mirrors:
+ * which = 0 sqg_range, 1 sqg_layout, 2 sqg_qkv_args, 3 sqg_attn_args; else -1. */
+SQG_API int64_t sqg_struct_size(int which);
+
+/* Host only.  Row chunks of `size` rows over [0, n); a last chunk shorter than
+ * `min_tail` joins the previous one; size <= 0 or size >= n gives one chunk
+ * ([VL] helpers section, `_ranges`).  Writes at most `cap` (begin, end) pairs to
+ * `begins`/`ends` (host) and the total count to *count. */
+SQG_API int sqg_chunk_ranges(int64_t n, int64_t size, int64_t min_tail, int64_t* begins,
+                             int64_t* ends, int32_t cap, int32_t* count);
+
+/* Host only.  Validates a token-range precision policy ([FR] "Mixed precision for
+ * conditioning") and fills the packed-store layout.  Ranges must be sorted,
+ * contiguous, non-empty, cover [0, n_tokens), have interior boundaries that are
+ * multiples of 128, and number at most SQG_MAX_SEGMENTS; n_ranges 0 = all INT4.
+ * d_model must be 128 * n_heads. */
+SQG_API int sqg_kv_layout(int64_t n_tokens, int32_t d_model, int32_t n_heads,
+                          const sqg_range* ranges, int32_t n_ranges, sqg_layout* out);
+
+/* Host only.  Split-half RoPE tables for positions [pos0, pos0 + n): cos and sin of
+ * pos * theta^(-2i/128), i in [0, 64), computed in fp64 and rounded to fp32, into the
+ * host arrays cos_out / sin_out ([n, 64] each). */
+SQG_API int sqg_rope_table(int64_t pos0, int64_t n, double theta, float* cos_out, float* sin_out);
+
+/* The streamed QKV projection with its quantising epilogue ([FR] "Proposed backend
+ * capability"; [VL] block section `_phase1_kv`).  For the rows of each chunk of
+ * `chunk_rows` it computes y = x W (bf16 inputs, fp32 accumulation), never storing
+ * the fused [N, 3d] tensor:
+ *   - q = y[:, 0:d], k = y[:, d:2d], v = y[:, 2d:3d], per head of 128;
+ *   - if norm weights are given: per-head RMSNorm of q and k; if RoPE tables are
+ *     given: split-half RoPE of q and k ([VL] helpers `_norm_rope`);
+ *   - Q = bf16(q) stored in the model basis;
+ *   - K and V: r = u H / sqrt(128) (Sylvester Hadamard, [VL] kvi8r `_hadamard`),
+ *     per group of 32: s = fp16(max|r| / qmax), code = clamp(rne(r / s), +-qmax)
+ *     (qmax 7 for INT4, 127 for INT8 ranges), packed per sqg_kv_layout.
+ * Chunks only partition the launches: results do not depend on chunk_rows. */
+SQG_API int sqg_streamed_qkv_quant(const sqg_qkv_args* args, void* stream);
+
+/* Flash-style attention that reads the packed K/V tile by tile ([FR] "Proposed
+ * backend capability", "Dense fallback is important"; [VL] kvi8r
+ * `_blockwise_attention_q`): each query tile is rotated once by H/sqrt(128),
+ * scores and P.V run against K/V dequantised in on-chip memory in the rotated
+ * basis, blocks combine by online softmax, and the output is rotated back once.
+ * Non-causal, no mask.  O = softmax(scale * Q K^T) V and lse = ln sum exp(scale * Q K^T)
+ * over keys [kv_begin, kv_end).  With kv_block > 0 the keys are processed in
+ * blocks whose partial (O, lse) are merged as in [VL] kvi8r `_online_combine`;
+ * accumulate = 1 merges into the (O, lse) already in the buffers (requires
+ * o_dtype SQG_F32). */
+SQG_API int sqg_packed_kv_attention(const sqg_attn_args* args, void* stream);
+
+/* Test entry: runs the kernels' own quantise-and-pack step on fp32 rotated vectors
+ * r (device, [rows, 128]) with format fmt for every row; writes codes (device,
+ * [rows, 64] bytes for INT4 or [rows, 128] for INT8) and scales (device, fp16
+ * [rows, 4]).  rows >= 0. */
+SQG_API int sqg_test_quant_pack_f32(const float* r, int64_t rows, int32_t fmt, void* codes,
+                                    void* scales, void* stream);
+
+/* Test entry: runs the kernels' own in-register 128-point Hadamard butterfly on
+ * in (device, fp32 [rows, 128]) into out; normalize = 1 multiplies by 1/sqrt(128). */
+SQG_API int sqg_test_fwht_f32(const float* in, float* out, int64_t rows, int32_t normalize,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SQG_H */

@@ -1,0 +1,276 @@
+"""ctypes binding of libsqg.so.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Torch supplies device memory (tensor storage) and the current HIP
+stream.  There is no CPU fallback: if libsqg.so is missing or a tensor is not on
+the GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence, Tuple
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libsqg.so")
+
+SQG_INT4_ROT = 0
+SQG_INT8_ROT = 1
+SQG_F32, SQG_BF16, SQG_F16 = 0, 1, 2
+MAX_SEGMENTS = 16
+HEAD_DIM = 128
+
+_c_i64 = ctypes.c_int64
+_c_i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
+
+
+class SqgError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("sqg status %d: %s" % (status, message))
+        self.status = status
+
+
+class Range(ctypes.Structure):
+    _fields_ = [("begin", _c_i64), ("end", _c_i64), ("fmt", _c_i32), ("reserved", _c_i32)]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("n_tokens", _c_i64), ("n_heads", _c_i32), ("n_segments", _c_i32),
+                ("seg_begin", _c_i64 * MAX_SEGMENTS), ("seg_end", _c_i64 * MAX_SEGMENTS),
+                ("seg_offset", _c_i64 * MAX_SEGMENTS), ("seg_fmt", _c_i32 * MAX_SEGMENTS),
+                ("seg_row_bytes", _c_i32 * MAX_SEGMENTS), ("q_bytes", _c_i64),
+                ("pack_bytes", _c_i64), ("scale_bytes", _c_i64), ("bf16_qkv_bytes", _c_i64)]
+
+
+class QkvArgs(ctypes.Structure):
+    _fields_ = [("n_tokens", _c_i64), ("d_model", _c_i32), ("n_heads", _c_i32),
+                ("x", _vp), ("ldx", _c_i64), ("w_qkv", _vp), ("ldw", _c_i64),
+                ("q_norm_w", _vp), ("k_norm_w", _vp), ("eps", ctypes.c_float),
+                ("rope_cos", _vp), ("rope_sin", _vp),
+                ("ranges", ctypes.POINTER(Range)), ("n_ranges", _c_i32), ("reserved", _c_i32),
+                ("chunk_rows", _c_i64), ("min_tail", _c_i64),
+                ("q", _vp), ("ldq", _c_i64), ("kpack", _vp), ("vpack", _vp),
+                ("kscale", _vp), ("vscale", _vp)]
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [("n_tokens", _c_i64), ("d_model", _c_i32), ("n_heads", _c_i32),
+                ("q", _vp), ("ldq", _c_i64), ("kpack", _vp), ("vpack", _vp),
+                ("kscale", _vp), ("vscale", _vp),
+                ("ranges", ctypes.POINTER(Range)), ("n_ranges", _c_i32), ("o_dtype", _c_i32),
+                ("q_begin", _c_i64), ("q_end", _c_i64), ("kv_begin", _c_i64), ("kv_end", _c_i64),
+                ("kv_block", _c_i64), ("accumulate", _c_i32), ("softmax_scale", ctypes.c_float),
+                ("o", _vp), ("ldo", _c_i64), ("lse", _vp)]
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None):
+    """Load libsqg.so (built by __graft_entry__.build() / streamed_qkv_gemm_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError("libsqg.so not found at %s: build it first with "
+                           "`python -m streamed_qkv_gemm_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    lib.sqg_version.restype = ctypes.c_int
+    lib.sqg_status_string.restype = ctypes.c_char_p
+    lib.sqg_status_string.argtypes = [ctypes.c_int]
+    lib.sqg_last_error.restype = ctypes.c_char_p
+    lib.sqg_struct_size.restype = _c_i64
+    lib.sqg_struct_size.argtypes = [ctypes.c_int]
+    lib.sqg_chunk_ranges.argtypes = [_c_i64, _c_i64, _c_i64, ctypes.POINTER(_c_i64),
+                                     ctypes.POINTER(_c_i64), _c_i32, ctypes.POINTER(_c_i32)]
+    lib.sqg_kv_layout.argtypes = [_c_i64, _c_i32, _c_i32, ctypes.POINTER(Range), _c_i32,
+                                  ctypes.POINTER(Layout)]
+    lib.sqg_rope_table.argtypes = [_c_i64, _c_i64, ctypes.c_double, _vp, _vp]
+    lib.sqg_streamed_qkv_quant.argtypes = [ctypes.POINTER(QkvArgs), _vp]
+    lib.sqg_packed_kv_attention.argtypes = [ctypes.POINTER(AttnArgs), _vp]
+    lib.sqg_test_quant_pack_f32.argtypes = [_vp, _c_i64, _c_i32, _vp, _vp, _vp]
+    lib.sqg_test_fwht_f32.argtypes = [_vp, _vp, _c_i64, _c_i32, _vp]
+    for name, cls in ((0, Range), (1, Layout), (2, QkvArgs), (3, AttnArgs)):
+        got = lib.sqg_struct_size(name)
+        if got != ctypes.sizeof(cls):
+            raise RuntimeError("ABI mismatch: %s is %d bytes in the library, %d in the binding"
+                               % (cls.__name__, got, ctypes.sizeof(cls)))
+    _lib = lib
+    return lib
+
+
+def lib_path() -> str:
+    return LIB_PATH
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load()
+        raise SqgError(status, lib.sqg_last_error().decode())
+
+
+def _ranges_array(ranges: Optional[Sequence[Tuple[int, int, int]]]):
+    if not ranges:
+        return None, 0
+    arr = (Range * len(ranges))()
+    for i, (b, e, f) in enumerate(ranges):
+        arr[i].begin, arr[i].end, arr[i].fmt, arr[i].reserved = int(b), int(e), int(f), 0
+    return arr, len(ranges)
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev_ptr(t: Optional[torch.Tensor], name: str) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor (the library has no CPU path)" % name)
+    return t.data_ptr()
+
+
+def version() -> int:
+    return load().sqg_version()
+
+
+def chunk_ranges(n: int, size: int, min_tail: int = 512):
+    lib = load()
+    count = _c_i32(0)
+    _check(lib.sqg_chunk_ranges(n, size, min_tail, None, None, 0, ctypes.byref(count)))
+    cap = count.value
+    b = (_c_i64 * max(cap, 1))()
+    e = (_c_i64 * max(cap, 1))()
+    _check(lib.sqg_chunk_ranges(n, size, min_tail, b, e, cap, ctypes.byref(count)))
+    return [(b[i], e[i]) for i in range(count.value)]
+
+
+def kv_layout(n_tokens: int, d_model: int, ranges=None) -> Dict:
+    lib = load()
+    arr, nr = _ranges_array(ranges)
+    L = Layout()
+    _check(lib.sqg_kv_layout(n_tokens, d_model, d_model // HEAD_DIM, arr, nr, ctypes.byref(L)))
+    segs = [{"begin": L.seg_begin[i], "end": L.seg_end[i], "fmt": L.seg_fmt[i],
+             "offset": L.seg_offset[i], "row_bytes": L.seg_row_bytes[i]} for i in range(L.n_segments)]
+    return {"n_tokens": L.n_tokens, "n_heads": L.n_heads, "segments": segs,
+            "q_bytes": L.q_bytes, "pack_bytes": L.pack_bytes, "scale_bytes": L.scale_bytes,
+            "bf16_qkv_bytes": L.bf16_qkv_bytes}
+
+
+def rope_table(n_tokens: int, theta: float = 10000.0, pos0: int = 0, device="cuda"):
+    """fp32 [N, 64] cos and sin tables built by the library on the host (fp64 -> fp32)."""
+    lib = load()
+    cos = torch.empty((n_tokens, 64), dtype=torch.float32)
+    sin = torch.empty((n_tokens, 64), dtype=torch.float32)
+    _check(lib.sqg_rope_table(pos0, n_tokens, theta, cos.data_ptr(), sin.data_ptr()))
+    return cos.to(device), sin.to(device)
+
+
+def alloc_store(n_tokens: int, d_model: int, ranges=None, device="cuda"):
+    """Empty output buffers of the streamed QKV-quant: Q, packed K/V and scales."""
+    L = kv_layout(n_tokens, d_model, ranges)
+    H = d_model // HEAD_DIM
+    return {
+        "q": torch.empty((n_tokens, d_model), dtype=torch.bfloat16, device=device),
+        "kpack": torch.empty((max(L["pack_bytes"], 16),), dtype=torch.uint8, device=device),
+        "vpack": torch.empty((max(L["pack_bytes"], 16),), dtype=torch.uint8, device=device),
+        "kscale": torch.empty((H, n_tokens, 4), dtype=torch.float16, device=device),
+        "vscale": torch.empty((H, n_tokens, 4), dtype=torch.float16, device=device),
+        "layout": L,
+        "ranges": list(ranges) if ranges else None,
+    }
+
+
+def streamed_qkv_quant(x: torch.Tensor, w_qkv: torch.Tensor, ranges=None, chunk_rows: int = 0,
+                       min_tail: int = 512, q_norm_w: Optional[torch.Tensor] = None,
+                       k_norm_w: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                       rope_cos: Optional[torch.Tensor] = None,
+                       rope_sin: Optional[torch.Tensor] = None, out: Optional[Dict] = None):
+    """streamed_qkv_quant(x, W_qkv, range_policy) -> {q, kpack, vpack, kscale, vscale}.
+
+    x bf16 [N, d], w_qkv bf16 [d, 3d] row-major.  Enqueued on the current stream."""
+    lib = load()
+    N, d = x.shape
+    if out is None:
+        out = alloc_store(N, d, ranges, device=x.device)
+    arr, nr = _ranges_array(ranges)
+    a = QkvArgs()
+    a.n_tokens, a.d_model, a.n_heads = N, d, d // HEAD_DIM
+    a.x, a.ldx = _dev_ptr(x, "x"), x.stride(0)
+    a.w_qkv, a.ldw = _dev_ptr(w_qkv, "w_qkv"), w_qkv.stride(0)
+    a.q_norm_w, a.k_norm_w = _dev_ptr(q_norm_w, "q_norm_w"), _dev_ptr(k_norm_w, "k_norm_w")
+    a.eps = eps
+    a.rope_cos, a.rope_sin = _dev_ptr(rope_cos, "rope_cos"), _dev_ptr(rope_sin, "rope_sin")
+    a.ranges = ctypes.cast(arr, ctypes.POINTER(Range)) if arr is not None else None
+    a.n_ranges, a.reserved = nr, 0
+    a.chunk_rows, a.min_tail = chunk_rows, min_tail
+    a.q, a.ldq = _dev_ptr(out["q"], "q"), out["q"].stride(0)
+    a.kpack, a.vpack = _dev_ptr(out["kpack"], "kpack"), _dev_ptr(out["vpack"], "vpack")
+    a.kscale, a.vscale = _dev_ptr(out["kscale"], "kscale"), _dev_ptr(out["vscale"], "vscale")
+    for t, nm in ((x, "x"), (w_qkv, "w_qkv")):
+        if t.dtype != torch.bfloat16 or t.stride(-1) != 1:
+            raise ValueError("%s must be a row-major bf16 tensor" % nm)
+    _check(lib.sqg_streamed_qkv_quant(ctypes.byref(a), _stream(x.device)))
+    return out
+
+
+_ODT = {torch.float32: SQG_F32, torch.bfloat16: SQG_BF16, torch.float16: SQG_F16}
+
+
+def packed_kv_attention(store: Dict, q: Optional[torch.Tensor] = None, q_begin: int = 0,
+                        q_end: int = 0, kv_begin: int = 0, kv_end: int = 0, kv_block: int = 0,
+                        accumulate: bool = False, o: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None, o_dtype=torch.float32,
+                        softmax_scale: float = 0.0, want_lse: bool = True):
+    """packed_kv_attention(Q, Kpack, Vpack, scales) -> (O, lse).
+
+    `store` is what streamed_qkv_quant returned (or the same keys).  O is [N, d]
+    in the model basis; lse is fp32 [H, N] (natural log)."""
+    lib = load()
+    q = store["q"] if q is None else q
+    N, d = q.shape
+    H = d // HEAD_DIM
+    if o is None:
+        o = torch.empty((N, d), dtype=o_dtype, device=q.device)
+    if lse is None and (want_lse or accumulate or kv_block > 0):
+        lse = torch.empty((H, N), dtype=torch.float32, device=q.device)
+    arr, nr = _ranges_array(store.get("ranges"))
+    a = AttnArgs()
+    a.n_tokens, a.d_model, a.n_heads = N, d, H
+    a.q, a.ldq = _dev_ptr(q, "q"), q.stride(0)
+    a.kpack, a.vpack = _dev_ptr(store["kpack"], "kpack"), _dev_ptr(store["vpack"], "vpack")
+    a.kscale, a.vscale = _dev_ptr(store["kscale"], "kscale"), _dev_ptr(store["vscale"], "vscale")
+    a.ranges = ctypes.cast(arr, ctypes.POINTER(Range)) if arr is not None else None
+    a.n_ranges = nr
+    a.o_dtype = _ODT[o.dtype]
+    a.q_begin, a.q_end, a.kv_begin, a.kv_end = q_begin, q_end, kv_begin, kv_end
+    a.kv_block, a.accumulate, a.softmax_scale = kv_block, int(bool(accumulate)), softmax_scale
+    a.o, a.ldo = _dev_ptr(o, "o"), o.stride(0)
+    a.lse = _dev_ptr(lse, "lse")
+    _check(lib.sqg_packed_kv_attention(ctypes.byref(a), _stream(q.device)))
+    return o, lse
+
+
+def test_quant_pack_f32(r: torch.Tensor, fmt: int):
+    """The kernels' quantise/pack step on fp32 rotated rows r [rows, 128] (GPU)."""
+    lib = load()
+    rows = r.shape[0]
+    rb = 64 if fmt == SQG_INT4_ROT else 128
+    codes = torch.empty((rows, rb), dtype=torch.uint8, device=r.device)
+    scales = torch.empty((rows, 4), dtype=torch.float16, device=r.device)
+    _check(lib.sqg_test_quant_pack_f32(_dev_ptr(r, "r"), rows, fmt, codes.data_ptr(),
+                                       scales.data_ptr(), _stream(r.device)))
+    return codes, scales
+
+
+def test_fwht_f32(x: torch.Tensor, normalize: bool = False):
+    """The kernels' 128-point Hadamard butterfly on fp32 rows x [rows, 128] (GPU)."""
+    lib = load()
+    out = torch.empty_like(x)
+    _check(lib.sqg_test_fwht_f32(_dev_ptr(x, "x"), out.data_ptr(), x.shape[0], int(normalize),
+                                 _stream(x.device)))
+    return out

@@ -1,0 +1,441 @@
+// Flash-style attention over a packed rotated INT4/INT8 K/V store, for gfx950.
+//
+// Feature request "Streamed QKV Projection and Packed Low-Bit K/V Support",
+// sections "Proposed backend capability" and "Dense fallback is important":
+// attention consumes Q in bf16 and K/V as packed low-bit codes, decoding K/V
+// only tile by tile inside the kernel.  VRAM Lab page, kvi8r section
+// (`_Int8KV`, `_blockwise_attention_q`, `_online_combine`): K/V stay in the
+// orthonormal Hadamard basis; the query tile is rotated once, scores and P.V run
+// in that basis (q.k = (qH).(kH), P.V = (P.(VH)).H^T), partial results combine by
+// online softmax, and the output is rotated back once.  That page also measured
+// that the rotated basis needs fp16 operands rather than bf16 (rotation spreads
+// every value to the same magnitude), so both products use f16 MFMA with fp32
+// accumulation.
+//
+// Workgroup: 256 queries of one head, four waves of 64 queries.  Per 64-key tile
+// the workgroup loads the packed codes and fp16 scales once, dequantises them to
+// f16 in LDS (K row-major, V transposed), and every wave computes
+//   S^T = K_r Q_r^T        (keys x queries, 32x32x16 f16 MFMA)
+//   online softmax down each query column (one lane-pair exchange per tile)
+//   O^T += V_r^T P^T       (dims x queries)
+// The transposed products keep a query's scores and its 128 output values in one
+// lane pair, so the softmax statistics and the final inverse rotation are
+// register-local apart from one exchange with lane ^ 32.
+#include "device_common.h"
+#include "internal.h"
+
+namespace sqg {
+namespace {
+
+constexpr int kBQ = 256;              // queries per workgroup
+constexpr int kBKV = 64;              // keys per tile
+constexpr int kKStride = 128 + 8;     // f16 per K row in LDS (272 B)
+constexpr int kVStride = kBKV + 8;    // f16 per transposed V row in LDS (144 B)
+constexpr int kKTile = kBKV * kKStride;
+constexpr int kVTile = 128 * kVStride;
+
+// position of key k (0..63) inside a transposed V row: bits 2 and 3 are swapped so
+// that the 8 keys one lane feeds to a 16-key MFMA step are contiguous
+__device__ __forceinline__ int vpos(int k) {
+  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+// 8 f16 values code * scale from 8 INT4 codes (one dword, code j in bits 4j..4j+3)
+__device__ __forceinline__ void dequant_int4x8(uint32_t w, uint32_t s2, uint32_t (&out)[4]) {
+  const uint32_t b = w ^ 0x88888888u;          // nibble = code + 8
+  const uint32_t lo = b & 0x0f0f0f0fu;         // codes 0, 2, 4, 6 in bytes 0..3
+  const uint32_t hi = (b >> 4) & 0x0f0f0f0fu;  // codes 1, 3, 5, 7
+  const f16x2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const f16x2 sc = __builtin_bit_cast(f16x2, s2);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    // f16 bit pattern 0x6400 | u is 1024 + u exactly
+    const uint32_t sel = (uint32_t)p | 0x0c00u | ((uint32_t)(4 + p) << 16) | 0x0c000000u;
+    const uint32_t pr = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
+    f16x2 v = __builtin_bit_cast(f16x2, pr) + bias;  // exact code
+    v = v * sc;                                       // one rounding to f16
+    out[p] = __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+// 4 f16 values code * scale from 4 INT8 codes (one dword, code j in byte j)
+__device__ __forceinline__ void dequant_int8x4(uint32_t w, uint32_t s2, uint32_t (&out)[2]) {
+  const uint32_t b = w ^ 0x80808080u;  // byte = code + 128
+  const f16x2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  const f16x2 sc = __builtin_bit_cast(f16x2, s2);
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const uint32_t sel = (uint32_t)(2 * p) | 0x0c00u | ((uint32_t)(2 * p + 1) << 16) | 0x0c000000u;
+    const uint32_t pr = __builtin_amdgcn_perm(0u, b, sel) | 0x64006400u;
+    f16x2 v = __builtin_bit_cast(f16x2, pr) + bias;
+    v = v * sc;
+    out[p] = __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+struct TileRegs {
+  u32x4 k[2];      // K codes of one (key, group): 16 B INT4 or 32 B INT8
+  uint32_t kscale; // fp16 scale of that group
+  u32x2 v[4];      // V codes of 4 keys x 8 dims: 4 B INT4 or 8 B INT8 each
+  uint32_t vscale[4];
+  int fmt;
+};
+
+__global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnParams p) {
+  __shared__ __attribute__((aligned(16))) _Float16 sK[2][kKTile];
+  __shared__ __attribute__((aligned(16))) _Float16 sV[2][kVTile];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hsel = lane >> 5;
+  const int head = blockIdx.y;
+  const int64_t N = p.n_tokens;
+
+  // ---- query tile: rotate once, keep as f16 MFMA B operands
+  const int64_t qw0 = p.q_begin + (int64_t)blockIdx.x * kBQ + 64 * wave;
+  f16x8 qf[2][8];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int64_t row = qw0 + 32 * qb + l32;
+    const bool valid = row < p.q_end;
+    const uint16_t* src = p.q + (valid ? row : 0) * p.ldq + head * kHeadDim + 8 * hsel;
+    // element e(ks, j) = 16 ks + 8 hsel + j: bits 0-2 = j, bit 3 = lane pair, bits 4-6 = ks
+    float v[8][8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (valid) raw = *reinterpret_cast<const u32x4*>(src + 16 * ks);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[ks][2 * j] = bf16_lo(raw[j]);
+        v[ks][2 * j + 1] = bf16_hi(raw[j]);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int bit = 1; bit < 8; bit <<= 1)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (j & bit) continue;
+          const float x = v[ks][j], y = v[ks][j | bit];
+          v[ks][j] = x + y;
+          v[ks][j | bit] = x - y;
+        }
+#pragma unroll
+    for (int bit = 1; bit < 8; bit <<= 1)
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        if (ks & bit) continue;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x = v[ks][j], y = v[ks | bit][j];
+          v[ks][j] = x + y;
+          v[ks | bit][j] = x - y;
+        }
+      }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float pr = xor32(v[ks][j]);
+        const float r = hsel ? (pr - v[ks][j]) : (v[ks][j] + pr);
+        qf[qb][ks][j] = (_Float16)(r * kInvSqrtHeadDim);
+      }
+  }
+
+  // ---- per-thread maps for the K/V tile loads
+  const int kkey = tid >> 2;   // K: key of the tile, group (tid & 3)
+  const int kgrp = tid & 3;
+  const int vq = tid & 15;     // V: keys 4 vq .. 4 vq + 3, dims 8 vd .. 8 vd + 7
+  const int vd = tid >> 4;
+
+  auto load_tile = [&](int64_t key0, TileRegs& r) {
+    const int seg = find_segment(p.seg, key0);
+    const int fmt = p.seg.fmt[seg];
+    const int64_t sb = p.seg.begin[seg];
+    const int64_t slen = p.seg.end[seg] - sb;
+    const int64_t hrow = (int64_t)head * slen - sb;
+    r.fmt = fmt;
+    const int rb = fmt == FMT_INT4 ? 64 : 128;
+    const uint8_t* kb = p.kpack + p.seg.offset[seg];
+    const uint8_t* vb = p.vpack + p.seg.offset[seg];
+    {
+      const int64_t key = key0 + kkey;
+      const bool ok = key < p.kv_end;
+      const int64_t kk = ok ? key : key0;
+      const uint8_t* src = kb + (hrow + kk) * rb;
+      u32x4 z = {0u, 0u, 0u, 0u};
+      r.k[0] = z;
+      r.k[1] = z;
+      r.kscale = 0u;
+      if (ok) {
+        if (fmt == FMT_INT4) {
+          r.k[0] = *reinterpret_cast<const u32x4*>(src + 16 * kgrp);
+        } else {
+          r.k[0] = *reinterpret_cast<const u32x4*>(src + 32 * kgrp);
+          r.k[1] = *reinterpret_cast<const u32x4*>(src + 32 * kgrp + 16);
+        }
+        r.kscale = p.kscale[((int64_t)head * N + key) * 4 + kgrp];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t key = key0 + 4 * vq + j;
+      const bool ok = key < p.kv_end;
+      u32x2 z = {0u, 0u};
+      r.v[j] = z;
+      r.vscale[j] = 0u;
+      if (ok) {
+        const uint8_t* src = vb + (hrow + key) * rb;
+        if (fmt == FMT_INT4) {
+          r.v[j][0] = *reinterpret_cast<const uint32_t*>(src + 4 * vd);
+        } else {
+          r.v[j] = *reinterpret_cast<const u32x2*>(src + 8 * vd);
+        }
+        r.vscale[j] = p.vscale[((int64_t)head * N + key) * 4 + (vd >> 2)];
+      }
+    }
+  };
+
+  auto store_tile = [&](const TileRegs& r, int stage) {
+    _Float16* K = sK[stage];
+    _Float16* V = sV[stage];
+    const uint32_t ks2 = r.kscale | (r.kscale << 16);
+    // K: 32 values of (key, group) -> row kkey, elements 32 kgrp ..
+    if (r.fmt == FMT_INT4) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t o[4];
+        dequant_int4x8(r.k[0][w], ks2, o);
+        u32x4 ov = {o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<u32x4*>(K + kkey * kKStride + 32 * kgrp + 8 * w) = ov;
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        uint32_t o[2];
+        dequant_int8x4(r.k[w >> 2][w & 3], ks2, o);
+        u32x2 ov = {o[0], o[1]};
+        *reinterpret_cast<u32x2*>(K + kkey * kKStride + 32 * kgrp + 4 * w) = ov;
+      }
+    }
+    // V: 4 keys x 8 dims, written transposed: row = dim, 4 keys contiguous
+    _Float16 vals[4][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t s2 = r.vscale[j] | (r.vscale[j] << 16);
+      uint32_t o[4];
+      if (r.fmt == FMT_INT4) {
+        dequant_int4x8(r.v[j][0], s2, o);
+      } else {
+        uint32_t a[2], b[2];
+        dequant_int8x4(r.v[j][0], s2, a);
+        dequant_int8x4(r.v[j][1], s2, b);
+        o[0] = a[0]; o[1] = a[1]; o[2] = b[0]; o[3] = b[1];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f16x2 h2 = __builtin_bit_cast(f16x2, o[e]);
+        vals[j][2 * e] = h2[0];
+        vals[j][2 * e + 1] = h2[1];
+      }
+    }
+    const int pos = vpos(4 * vq);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      f16x4 col = {vals[0][e], vals[1][e], vals[2][e], vals[3][e]};
+      *reinterpret_cast<f16x4*>(V + (8 * vd + e) * kVStride + pos) = col;
+    }
+  };
+
+  // ---- state
+  f32x16 oacc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[a][b][e] = 0.0f;
+  float m_run[2] = {-INFINITY, -INFINITY};  // running max of scale*log2e*score
+  float l_run[2] = {0.0f, 0.0f};            // lane-partial running sum
+  const float c = p.scale_log2;
+
+  const int64_t kv0 = p.kv_begin;
+  const int n_tiles = (int)((p.kv_end - kv0 + kBKV - 1) / kBKV);
+  TileRegs regs;
+  load_tile(kv0, regs);
+  store_tile(regs, 0);
+  __syncthreads();
+
+  for (int it = 0; it < n_tiles; ++it) {
+    const int stage = it & 1;
+    const int64_t key0 = kv0 + (int64_t)it * kBKV;
+    if (it + 1 < n_tiles) load_tile(key0 + kBKV, regs);
+
+    // S^T = K Q^T for 64 keys x 64 queries of this wave
+    f32x16 s[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[a][b][e] = 0.0f;
+    const _Float16* K = sK[stage];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const f16x8 kf =
+            *reinterpret_cast<const f16x8*>(K + (32 * kb + l32) * kKStride + 16 * ks + 8 * hsel);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[qb][ks], s[kb][qb], 0, 0, 0);
+      }
+    }
+
+    // mask keys past the end (last tile only)
+    if (key0 + kBKV > p.kv_end) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t key = key0 + 32 * kb + 8 * (e >> 2) + 4 * hsel + (e & 3);
+          if (key >= p.kv_end) {
+            s[kb][0][e] = -INFINITY;
+            s[kb][1][e] = -INFINITY;
+          }
+        }
+    }
+
+    // online softmax down each query column; P^T as f16 B operands
+    f16x8 pf[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][qb][e]);
+      mx = fmaxf(mx, xor32(mx));
+      const float m_new = fmaxf(m_run[qb], mx * c);
+      const float alpha = exp2f(m_run[qb] - m_new);
+      m_run[qb] = m_new;
+      float lsum = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float pv = exp2f(s[kb][qb][e] * c - m_new);
+          lsum += pv;
+          pf[qb][2 * kb + (e >> 3)][e & 7] = (_Float16)pv;
+        }
+      l_run[qb] = l_run[qb] * alpha + lsum;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][qb][e] *= alpha;
+    }
+
+    // O^T += V^T P^T
+    const _Float16* V = sV[stage];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const f16x8 vf =
+            *reinterpret_cast<const f16x8*>(V + (32 * db + l32) * kVStride + 16 * ks + 8 * hsel);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[qb][ks], oacc[db][qb], 0, 0, 0);
+      }
+    }
+
+    if (it + 1 < n_tiles) store_tile(regs, stage ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalise, rotate back, merge, store
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int64_t row = qw0 + 32 * qb + l32;
+    const bool valid = row < p.q_end;
+    const float l_tot = l_run[qb] + xor32(l_run[qb]);
+    const float inv = 1.0f / l_tot;
+    float u[4][16];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) u[db][e] = oacc[db][qb][e] * inv;
+    fwht128_cols(u);
+    float lse = (m_run[qb] + log2f(l_tot)) * 0.6931471805599453f;
+    const int64_t rr = valid ? row : 0;
+    if (p.accumulate) {
+      const float* orow = reinterpret_cast<const float*>(p.o) + rr * p.ldo + head * kHeadDim + 4 * hsel;
+      const float lse_old = p.lse[(int64_t)head * N + rr];
+      const float mx = fmaxf(lse_old, lse);
+      const float lse_new = mx + logf(expf(lse_old - mx) + expf(lse - mx));
+      const float w_old = expf(lse_old - lse_new);
+      const float w_new = expf(lse - lse_new) * kInvSqrtHeadDim;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4 prev = {0.f, 0.f, 0.f, 0.f};
+          if (valid) prev = *reinterpret_cast<const f32x4*>(orow + 32 * db + 8 * q);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) u[db][4 * q + j] = prev[j] * w_old + u[db][4 * q + j] * w_new;
+        }
+      lse = lse_new;
+    } else {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) u[db][e] *= kInvSqrtHeadDim;
+    }
+    if (valid) {
+      if (p.o_dtype == 0) {
+        float* orow = reinterpret_cast<float*>(p.o) + row * p.ldo + head * kHeadDim + 4 * hsel;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            f32x4 v = {u[db][4 * q], u[db][4 * q + 1], u[db][4 * q + 2], u[db][4 * q + 3]};
+            *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * q) = v;
+          }
+      } else {
+        uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + row * p.ldo + head * kHeadDim + 4 * hsel;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            u32x2 v;
+            if (p.o_dtype == 1) {
+              v[0] = f32_to_bf16_bits(u[db][4 * q]) | (f32_to_bf16_bits(u[db][4 * q + 1]) << 16);
+              v[1] = f32_to_bf16_bits(u[db][4 * q + 2]) | (f32_to_bf16_bits(u[db][4 * q + 3]) << 16);
+            } else {
+              v[0] = f32_to_f16_bits(u[db][4 * q]) | (f32_to_f16_bits(u[db][4 * q + 1]) << 16);
+              v[1] = f32_to_f16_bits(u[db][4 * q + 2]) | (f32_to_f16_bits(u[db][4 * q + 3]) << 16);
+            }
+            *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * q) = v;
+          }
+      }
+      if (p.lse && hsel == 0) p.lse[(int64_t)head * N + row] = lse;
+    }
+  }
+}
+
+}  // namespace
+
+int launch_packed_attention(const AttnParams& p, void* stream) {
+  const int64_t nq = p.q_end - p.q_begin;
+  if (nq <= 0 || p.kv_end <= p.kv_begin) return 0;
+  const int64_t tiles = (nq + kBQ - 1) / kBQ;
+  hipLaunchKernelGGL(packed_attention_kernel, dim3((unsigned)tiles, (unsigned)p.n_heads), dim3(256),
+                     0, (hipStream_t)stream, p);
+  return (int)hipGetLastError();
+}
+
+}  // namespace sqg

@@ -1,0 +1,354 @@
+// C-ABI entry points of libsqg.so: argument checking, the packed-store layout, the
+// token-range policy, the row-chunk scheduler and the launch loops.  Plain C++17
+// with no HIP headers: every check runs on the host before anything is enqueued,
+// and the kernels are reached only through the launchers in internal.h.
+#define SQG_BUILDING_LIBRARY 1
+#include "../../include/sqg.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SQG_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Row chunks of `size` over [0, n), last chunk shorter than min_tail folded into the
+// previous one (VRAM Lab page, helpers section, `_ranges`).
+std::vector<std::pair<int64_t, int64_t>> chunk_plan(int64_t n, int64_t size, int64_t min_tail) {
+  std::vector<std::pair<int64_t, int64_t>> out;
+  if (size <= 0 || size >= n) {
+    out.emplace_back(0, n);
+    return out;
+  }
+  for (int64_t a = 0; a < n; a += size) out.emplace_back(a, a + size < n ? a + size : n);
+  if (out.size() > 1 && out.back().second - out.back().first < min_tail) {
+    out.pop_back();
+    out.back().second = n;
+  }
+  return out;
+}
+
+int build_layout(int64_t n, int32_t d, int32_t heads, const sqg_range* ranges, int32_t n_ranges,
+                 sqg_layout* L) {
+  if (n < 0) return fail(SQG_ERR_INVALID_ARGUMENT, "n_tokens must be >= 0 (got %lld)", (long long)n);
+  if (heads < 1 || d != heads * SQG_HEAD_DIM)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "d_model (%d) must equal 128 * n_heads (%d)", d, heads);
+  if (n_ranges < 0 || n_ranges > SQG_MAX_SEGMENTS)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "n_ranges must be in [0, %d] (got %d)", SQG_MAX_SEGMENTS,
+                n_ranges);
+  if (n_ranges > 0 && !ranges) return fail(SQG_ERR_INVALID_ARGUMENT, "ranges is NULL");
+  std::memset(L, 0, sizeof *L);
+  L->n_tokens = n;
+  L->n_heads = heads;
+  if (n_ranges == 0) {
+    if (n > 0) {
+      L->n_segments = 1;
+      L->seg_begin[0] = 0;
+      L->seg_end[0] = n;
+      L->seg_fmt[0] = SQG_INT4_ROT;
+    }
+  } else {
+    int64_t pos = 0;
+    for (int i = 0; i < n_ranges; ++i) {
+      const sqg_range& r = ranges[i];
+      if (r.fmt != SQG_INT4_ROT && r.fmt != SQG_INT8_ROT)
+        return fail(SQG_ERR_INVALID_ARGUMENT, "range %d: unknown format %d", i, r.fmt);
+      if (r.reserved != 0) return fail(SQG_ERR_INVALID_ARGUMENT, "range %d: reserved field not 0", i);
+      if (r.begin != pos)
+        return fail(SQG_ERR_INVALID_ARGUMENT,
+                    "range %d begins at %lld, expected %lld (ranges must be sorted and contiguous)",
+                    i, (long long)r.begin, (long long)pos);
+      if (r.end <= r.begin)
+        return fail(SQG_ERR_INVALID_ARGUMENT, "range %d is empty or reversed", i);
+      if (r.end < n && r.end % 128 != 0)
+        return fail(SQG_ERR_INVALID_ARGUMENT, "range %d: interior boundary %lld is not a multiple of 128",
+                    i, (long long)r.end);
+      L->seg_begin[i] = r.begin;
+      L->seg_end[i] = r.end;
+      L->seg_fmt[i] = r.fmt;
+      pos = r.end;
+    }
+    if (pos != n)
+      return fail(SQG_ERR_INVALID_ARGUMENT, "ranges end at %lld, not at n_tokens %lld", (long long)pos,
+                  (long long)n);
+    L->n_segments = n_ranges;
+  }
+  int64_t off = 0;
+  for (int s = 0; s < L->n_segments; ++s) {
+    L->seg_row_bytes[s] = L->seg_fmt[s] == SQG_INT4_ROT ? 64 : 128;
+    L->seg_offset[s] = off;
+    off += (int64_t)heads * (L->seg_end[s] - L->seg_begin[s]) * L->seg_row_bytes[s];
+  }
+  L->pack_bytes = off;
+  L->scale_bytes = n * heads * 4 * 2;
+  L->q_bytes = n * (int64_t)d * 2;
+  L->bf16_qkv_bytes = 3 * L->q_bytes;
+  return SQG_OK;
+}
+
+sqg::SegTable seg_table(const sqg_layout& L) {
+  sqg::SegTable t;
+  std::memset(&t, 0, sizeof t);
+  t.n = L.n_segments;
+  for (int s = 0; s < L.n_segments; ++s) {
+    t.fmt[s] = L.seg_fmt[s];
+    t.begin[s] = L.seg_begin[s];
+    t.end[s] = L.seg_end[s];
+    t.offset[s] = L.seg_offset[s];
+  }
+  return t;
+}
+
+int launch_status(int hip_err, const char* what) {
+  if (hip_err != 0)
+    return fail(SQG_ERR_HIP, "%s: HIP error %d (%s)", what, hip_err, sqg::hip_error_text(hip_err));
+  return SQG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+SQG_API int sqg_version(void) { return SQG_VERSION; }
+
+SQG_API const char* sqg_status_string(int status) {
+  switch (status) {
+    case SQG_OK: return "ok";
+    case SQG_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SQG_ERR_UNSUPPORTED: return "unsupported shape";
+    case SQG_ERR_MISALIGNED: return "misaligned pointer or stride";
+    case SQG_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+SQG_API const char* sqg_last_error(void) { return g_last_error.c_str(); }
+
+SQG_API int64_t sqg_struct_size(int which) {
+  switch (which) {
+    case 0: return (int64_t)sizeof(sqg_range);
+    case 1: return (int64_t)sizeof(sqg_layout);
+    case 2: return (int64_t)sizeof(sqg_qkv_args);
+    case 3: return (int64_t)sizeof(sqg_attn_args);
+    default: return -1;
+  }
+}
+
+SQG_API int sqg_chunk_ranges(int64_t n, int64_t size, int64_t min_tail, int64_t* begins,
+                             int64_t* ends, int32_t cap, int32_t* count) {
+  if (n < 0) return fail(SQG_ERR_INVALID_ARGUMENT, "n must be >= 0");
+  if (!count) return fail(SQG_ERR_INVALID_ARGUMENT, "count is NULL");
+  if (cap > 0 && (!begins || !ends)) return fail(SQG_ERR_INVALID_ARGUMENT, "output arrays are NULL");
+  const auto plan = chunk_plan(n, size, min_tail);
+  *count = (int32_t)plan.size();
+  for (size_t i = 0; i < plan.size() && (int32_t)i < cap; ++i) {
+    begins[i] = plan[i].first;
+    ends[i] = plan[i].second;
+  }
+  return ok();
+}
+
+SQG_API int sqg_kv_layout(int64_t n_tokens, int32_t d_model, int32_t n_heads,
+                          const sqg_range* ranges, int32_t n_ranges, sqg_layout* out) {
+  if (!out) return fail(SQG_ERR_INVALID_ARGUMENT, "out is NULL");
+  const int st = build_layout(n_tokens, d_model, n_heads, ranges, n_ranges, out);
+  return st == SQG_OK ? ok() : st;
+}
+
+SQG_API int sqg_rope_table(int64_t pos0, int64_t n, double theta, float* cos_out, float* sin_out) {
+  if (n < 0 || pos0 < 0) return fail(SQG_ERR_INVALID_ARGUMENT, "n and pos0 must be >= 0");
+  if (n > 0 && (!cos_out || !sin_out)) return fail(SQG_ERR_INVALID_ARGUMENT, "output is NULL");
+  if (!(theta > 1.0)) return fail(SQG_ERR_INVALID_ARGUMENT, "theta must be > 1");
+  double inv[64];
+  for (int i = 0; i < 64; ++i) inv[i] = std::pow(theta, -2.0 * i / 128.0);
+  for (int64_t r = 0; r < n; ++r) {
+    const double pos = (double)(pos0 + r);
+    for (int i = 0; i < 64; ++i) {
+      const double a = pos * inv[i];
+      cos_out[r * 64 + i] = (float)std::cos(a);
+      sin_out[r * 64 + i] = (float)std::sin(a);
+    }
+  }
+  return ok();
+}
+
+SQG_API int sqg_streamed_qkv_quant(const sqg_qkv_args* a, void* stream) {
+  if (!a) return fail(SQG_ERR_INVALID_ARGUMENT, "args is NULL");
+  sqg_layout L;
+  int st = build_layout(a->n_tokens, a->d_model, a->n_heads, a->ranges, a->n_ranges, &L);
+  if (st != SQG_OK) return st;
+  const int64_t N = a->n_tokens;
+  const int64_t d = a->d_model;
+  if (d % 256 != 0)
+    return fail(SQG_ERR_UNSUPPORTED, "d_model must be a multiple of 256 (got %lld)", (long long)d);
+  if (a->reserved != 0) return fail(SQG_ERR_INVALID_ARGUMENT, "reserved field not 0");
+  if ((a->q_norm_w == nullptr) != (a->k_norm_w == nullptr))
+    return fail(SQG_ERR_INVALID_ARGUMENT, "q_norm_w and k_norm_w must both be set or both be NULL");
+  if ((a->rope_cos == nullptr) != (a->rope_sin == nullptr))
+    return fail(SQG_ERR_INVALID_ARGUMENT, "rope_cos and rope_sin must both be set or both be NULL");
+  if (a->q_norm_w && !(a->eps >= 0.0f && std::isfinite(a->eps)))
+    return fail(SQG_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if (a->chunk_rows < 0 || a->chunk_rows % 128 != 0)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "chunk_rows must be 0 or a positive multiple of 128 (got %lld)",
+                (long long)a->chunk_rows);
+  if (N == 0) return ok();
+  if (!a->x || !a->w_qkv || !a->q || !a->kpack || !a->vpack || !a->kscale || !a->vscale)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "a required device pointer is NULL");
+  if (a->ldx < d || a->ldw < 3 * d || a->ldq < d)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "row strides must be >= the row length (ldx %lld, ldw %lld, ldq %lld)",
+                (long long)a->ldx, (long long)a->ldw, (long long)a->ldq);
+  if (a->ldx % 8 || a->ldw % 8 || a->ldq % 8)
+    return fail(SQG_ERR_MISALIGNED, "row strides must be multiples of 8 elements");
+  const void* ptrs[] = {a->x, a->w_qkv, a->q, a->kpack, a->vpack, a->kscale, a->vscale,
+                        a->q_norm_w, a->k_norm_w, a->rope_cos, a->rope_sin};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(SQG_ERR_MISALIGNED, "device pointer %p is not 16-byte aligned", p);
+
+  sqg::QkvParams p;
+  std::memset(&p, 0, sizeof p);
+  p.x = static_cast<const uint16_t*>(a->x);
+  p.w = static_cast<const uint16_t*>(a->w_qkv);
+  p.q = static_cast<uint16_t*>(a->q);
+  p.kpack = static_cast<uint8_t*>(a->kpack);
+  p.vpack = static_cast<uint8_t*>(a->vpack);
+  p.kscale = static_cast<uint16_t*>(a->kscale);
+  p.vscale = static_cast<uint16_t*>(a->vscale);
+  p.q_norm_w = a->q_norm_w;
+  p.k_norm_w = a->k_norm_w;
+  p.rope_cos = a->rope_cos;
+  p.rope_sin = a->rope_sin;
+  p.ldx = a->ldx;
+  p.ldw = a->ldw;
+  p.ldq = a->ldq;
+  p.n_tokens = N;
+  p.d_model = a->d_model;
+  p.n_heads = a->n_heads;
+  p.eps = a->eps;
+  p.seg = seg_table(L);
+  const int64_t min_tail = a->min_tail < 0 ? 512 : a->min_tail;
+  for (const auto& c : chunk_plan(N, a->chunk_rows, min_tail)) {
+    p.row_begin = c.first;
+    p.row_end = c.second;
+    st = launch_status(sqg::launch_qkv_quant(p, stream), "streamed_qkv_quant launch");
+    if (st != SQG_OK) return st;
+  }
+  return ok();
+}
+
+SQG_API int sqg_packed_kv_attention(const sqg_attn_args* a, void* stream) {
+  if (!a) return fail(SQG_ERR_INVALID_ARGUMENT, "args is NULL");
+  sqg_layout L;
+  int st = build_layout(a->n_tokens, a->d_model, a->n_heads, a->ranges, a->n_ranges, &L);
+  if (st != SQG_OK) return st;
+  const int64_t N = a->n_tokens;
+  const int64_t d = a->d_model;
+  if (a->o_dtype != SQG_F32 && a->o_dtype != SQG_BF16 && a->o_dtype != SQG_F16)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "unknown o_dtype %d", a->o_dtype);
+  const int64_t q_end = a->q_end == 0 ? N : a->q_end;
+  const int64_t kv_end = a->kv_end == 0 ? N : a->kv_end;
+  if (a->q_begin < 0 || a->q_begin > q_end || q_end > N)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "query range [%lld, %lld) is outside [0, %lld]",
+                (long long)a->q_begin, (long long)q_end, (long long)N);
+  if (a->kv_block < 0 || a->kv_block % 128 != 0)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "kv_block must be 0 or a positive multiple of 128");
+  if (a->accumulate != 0 && a->accumulate != 1)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "accumulate must be 0 or 1");
+  if ((a->accumulate || a->kv_block > 0) && (!a->lse || a->o_dtype != SQG_F32))
+    return fail(SQG_ERR_INVALID_ARGUMENT,
+                "accumulate and kv_block > 0 need an lse buffer and o_dtype SQG_F32");
+  if (!(std::isfinite(a->softmax_scale) && a->softmax_scale >= 0.0f))
+    return fail(SQG_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+  if (N == 0 || q_end == a->q_begin) return ok();
+  if (a->kv_begin < 0 || a->kv_begin >= kv_end || kv_end > N)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "key range [%lld, %lld) is empty or outside [0, %lld]",
+                (long long)a->kv_begin, (long long)kv_end, (long long)N);
+  if (a->kv_begin % 128 != 0)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "kv_begin must be a multiple of 128");
+  if (!a->q || !a->kpack || !a->vpack || !a->kscale || !a->vscale || !a->o)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "a required device pointer is NULL");
+  if (a->ldq < d || a->ldo < d)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "row strides must be >= d_model");
+  if (a->ldq % 8 || a->ldo % 8) return fail(SQG_ERR_MISALIGNED, "row strides must be multiples of 8");
+  const void* ptrs[] = {a->q, a->kpack, a->vpack, a->kscale, a->vscale, a->o, a->lse};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(SQG_ERR_MISALIGNED, "device pointer %p is not 16-byte aligned", p);
+
+  sqg::AttnParams p;
+  std::memset(&p, 0, sizeof p);
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.kpack = static_cast<const uint8_t*>(a->kpack);
+  p.vpack = static_cast<const uint8_t*>(a->vpack);
+  p.kscale = static_cast<const uint16_t*>(a->kscale);
+  p.vscale = static_cast<const uint16_t*>(a->vscale);
+  p.o = a->o;
+  p.lse = a->lse;
+  p.ldq = a->ldq;
+  p.ldo = a->ldo;
+  p.n_tokens = N;
+  p.q_begin = a->q_begin;
+  p.q_end = q_end;
+  p.d_model = a->d_model;
+  p.n_heads = a->n_heads;
+  p.o_dtype = a->o_dtype;
+  const double scale = a->softmax_scale > 0.0f ? (double)a->softmax_scale : 1.0 / std::sqrt(128.0);
+  p.scale_log2 = (float)(scale * 1.4426950408889634);
+  p.seg = seg_table(L);
+  const auto blocks = chunk_plan(kv_end - a->kv_begin, a->kv_block, 512);
+  for (size_t i = 0; i < blocks.size(); ++i) {
+    p.kv_begin = a->kv_begin + blocks[i].first;
+    p.kv_end = a->kv_begin + blocks[i].second;
+    p.accumulate = (i == 0) ? a->accumulate : 1;
+    st = launch_status(sqg::launch_packed_attention(p, stream), "packed_kv_attention launch");
+    if (st != SQG_OK) return st;
+  }
+  return ok();
+}
+
+SQG_API int sqg_test_quant_pack_f32(const float* r, int64_t rows, int32_t fmt, void* codes,
+                                    void* scales, void* stream) {
+  if (rows < 0) return fail(SQG_ERR_INVALID_ARGUMENT, "rows must be >= 0");
+  if (fmt != SQG_INT4_ROT && fmt != SQG_INT8_ROT)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "unknown format %d", fmt);
+  if (rows == 0) return ok();
+  if (!r || !codes || !scales) return fail(SQG_ERR_INVALID_ARGUMENT, "a device pointer is NULL");
+  if (!aligned16(r) || !aligned16(codes) || ((uintptr_t)scales & 7u))
+    return fail(SQG_ERR_MISALIGNED, "r and codes must be 16-byte aligned, scales 8-byte aligned");
+  const int st = launch_status(sqg::launch_test_quant_pack(r, rows, fmt, codes, scales, stream),
+                               "test_quant_pack launch");
+  return st == SQG_OK ? ok() : st;
+}
+
+SQG_API int sqg_test_fwht_f32(const float* in, float* out, int64_t rows, int32_t normalize,
+                              void* stream) {
+  if (rows < 0) return fail(SQG_ERR_INVALID_ARGUMENT, "rows must be >= 0");
+  if (rows == 0) return ok();
+  if (!in || !out) return fail(SQG_ERR_INVALID_ARGUMENT, "a device pointer is NULL");
+  if (!aligned16(in) || !aligned16(out)) return fail(SQG_ERR_MISALIGNED, "pointers must be 16-byte aligned");
+  const int st = launch_status(sqg::launch_test_fwht(in, out, rows, normalize, stream), "test_fwht launch");
+  return st == SQG_OK ? ok() : st;
+}
+
+}  // extern "C"

@@ -1,0 +1,214 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol, and its
+host-side logic (chunk plan, range policy, layout, RoPE table, argument checks)
+agrees with the oracle.  No kernel is launched: every call here either is host-only
+or fails validation before the first launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import streamed_qkv_gemm_amd as sqg
+from streamed_qkv_gemm_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sqg.h")
+
+FAKE = 0x7f0000000000  # 16-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"SQG_API\s+[\w\s\*]+?\b(sqg_\w+)\s*\(", text)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sqg.load()
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sqg.version() == 100
+
+
+def test_struct_sizes_match_binding():
+    lib = sqg.load()
+    assert lib.sqg_struct_size(0) == ctypes.sizeof(B.Range)
+    assert lib.sqg_struct_size(1) == ctypes.sizeof(B.Layout)
+    assert lib.sqg_struct_size(2) == ctypes.sizeof(B.QkvArgs)
+    assert lib.sqg_struct_size(3) == ctypes.sizeof(B.AttnArgs)
+    assert lib.sqg_struct_size(9) == -1
+
+
+def test_status_strings():
+    lib = sqg.load()
+    assert lib.sqg_status_string(0) == b"ok"
+    assert lib.sqg_status_string(-3).startswith(b"misaligned")
+
+
+@pytest.mark.parametrize("n,size,tail", [(152263, 8192, 512), (16484, 8192, 512), (65536, 16384, 512),
+                                         (217088, 16384, 512), (1024, 0, 512), (100, 100, 512),
+                                         (0, 64, 512), (5000, 128, 0), (16896, 8192, 600)])
+def test_chunk_plan_matches_oracle(n, size, tail):
+    assert sqg.chunk_ranges(n, size, tail) == oracle.chunk_ranges(n, size, tail)
+
+
+def test_chunk_plan_random_matches_oracle():
+    rng = np.random.default_rng(1)
+    for _ in range(200):
+        n, size, tail = (int(v) for v in (rng.integers(0, 40000), rng.integers(-5, 9000),
+                                          rng.integers(0, 1000)))
+        assert sqg.chunk_ranges(n, size, tail) == oracle.chunk_ranges(n, size, tail)
+
+
+@pytest.mark.parametrize("n,d,ranges", [
+    (65536, 7168, [(0, 512, 1), (512, 8704, 1), (8704, 65536, 0)]),
+    (152263, 7168, None),
+    (1000, 512, [(0, 128, 1), (128, 1000, 0)]),
+    (777, 256, [(0, 256, 0), (256, 384, 1), (384, 777, 0)]),
+])
+def test_layout_matches_oracle(n, d, ranges):
+    L = sqg.kv_layout(n, d, ranges)
+    segs = oracle.range_segments(n, ranges)
+    ol, total = oracle.packed_layout(n, d // 128, segs)
+    assert L["pack_bytes"] == total
+    assert L["segments"] == ol
+    ws = oracle.working_set_bytes(n, d, segs)
+    assert L["q_bytes"] == ws["q"] and L["bf16_qkv_bytes"] == ws["bf16_qkv"]
+    assert L["scale_bytes"] == ws["k_scales"]
+
+
+@pytest.mark.parametrize("ranges", [
+    [(0, 512, 1), (640, 1024, 0)],
+    [(0, 640, 1), (512, 1024, 0)],
+    [(0, 500, 1), (500, 1024, 0)],
+    [(0, 512, 7), (512, 1024, 0)],
+    [(0, 512, 1), (512, 1000, 0)],
+    [(128, 1024, 0)],
+])
+def test_layout_rejects_bad_policies_like_the_oracle(ranges):
+    with pytest.raises(ValueError):
+        oracle.range_segments(1024, ranges)
+    with pytest.raises(sqg.SqgError) as e:
+        sqg.kv_layout(1024, 512, ranges)
+    assert e.value.status == -1
+    assert sqg.load().sqg_last_error()
+
+
+def test_layout_too_many_segments():
+    ranges = [(128 * i, 128 * (i + 1), i % 2) for i in range(17)]
+    with pytest.raises(sqg.SqgError):
+        sqg.kv_layout(128 * 17, 512, ranges)
+
+
+def test_rope_table_matches_oracle_angles():
+    lib = sqg.load()
+    n = 300
+    for pos0 in (0, 216788):
+        cos = np.zeros((n, 64), np.float32)
+        sin = np.zeros((n, 64), np.float32)
+        assert lib.sqg_rope_table(pos0, n, 10000.0, cos.ctypes.data, sin.ctypes.data) == 0
+        c, s = oracle.rope_angles(np.arange(pos0, pos0 + n))
+        assert np.max(np.abs(cos - c)) <= 6e-8 and np.max(np.abs(sin - s)) <= 6e-8
+
+
+# ----------------------------------------------------------------------------- argument checks
+def qkv_args(**kw):
+    a = B.QkvArgs()
+    a.n_tokens, a.d_model, a.n_heads = 1024, 512, 4
+    a.x, a.ldx, a.w_qkv, a.ldw = FAKE, 512, FAKE, 1536
+    a.q, a.ldq, a.kpack, a.vpack, a.kscale, a.vscale = FAKE, 512, FAKE, FAKE, FAKE, FAKE
+    a.eps, a.chunk_rows, a.min_tail = 1e-6, 0, 512
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def attn_args(**kw):
+    a = B.AttnArgs()
+    a.n_tokens, a.d_model, a.n_heads = 1024, 512, 4
+    a.q, a.ldq, a.kpack, a.vpack, a.kscale, a.vscale = FAKE, 512, FAKE, FAKE, FAKE, FAKE
+    a.o, a.ldo, a.lse = FAKE, 512, FAKE
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d_model=384, n_heads=3), -2),            # d not a multiple of 256
+    (dict(d_model=512, n_heads=3), -1),            # d != 128 H
+    (dict(n_tokens=-1), -1),
+    (dict(x=FAKE + 8), -3),                        # misaligned pointer
+    (dict(ldx=500), -1),                           # stride shorter than a row
+    (dict(ldq=516), -3),                           # stride not a multiple of 8
+    (dict(chunk_rows=100), -1),                    # chunk not a multiple of 128
+    (dict(chunk_rows=-128), -1),
+    (dict(x=None), -1),
+    (dict(q_norm_w=FAKE), -1),                     # q norm without k norm
+    (dict(rope_cos=FAKE), -1),                     # cos without sin
+    (dict(reserved=1), -1),
+])
+def test_qkv_argument_errors(kw, status):
+    lib = sqg.load()
+    a = qkv_args(**kw)
+    assert lib.sqg_streamed_qkv_quant(ctypes.byref(a), None) == status
+    assert len(lib.sqg_last_error()) > 0
+
+
+def test_qkv_bad_policy_rejected():
+    lib = sqg.load()
+    arr = (B.Range * 2)()
+    arr[0].begin, arr[0].end, arr[0].fmt = 0, 500, 1
+    arr[1].begin, arr[1].end, arr[1].fmt = 500, 1024, 0
+    a = qkv_args()
+    a.ranges, a.n_ranges = ctypes.cast(arr, ctypes.POINTER(B.Range)), 2
+    assert lib.sqg_streamed_qkv_quant(ctypes.byref(a), None) == -1
+    assert b"multiple of 128" in lib.sqg_last_error()
+
+
+def test_zero_tokens_is_a_noop():
+    lib = sqg.load()
+    a = qkv_args(n_tokens=0, x=None, w_qkv=None, q=None, kpack=None, vpack=None, kscale=None,
+                 vscale=None)
+    assert lib.sqg_streamed_qkv_quant(ctypes.byref(a), None) == 0
+    b = attn_args(n_tokens=0)
+    assert lib.sqg_packed_kv_attention(ctypes.byref(b), None) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o_dtype=5), -1),
+    (dict(q_begin=10, q_end=5), -1),
+    (dict(q_end=2000), -1),
+    (dict(kv_begin=64), -1),                       # kv_begin not a multiple of 128
+    (dict(kv_begin=512, kv_end=512), -1),          # empty key range
+    (dict(kv_block=100), -1),
+    (dict(accumulate=1, lse=None), -1),
+    (dict(kv_block=256, o_dtype=1), -1),           # merging needs fp32 O
+    (dict(softmax_scale=-1.0), -1),
+    (dict(o=FAKE + 4), -3),
+    (dict(ldo=500), -1),
+    (dict(kpack=None), -1),
+])
+def test_attention_argument_errors(kw, status):
+    lib = sqg.load()
+    a = attn_args(**kw)
+    assert lib.sqg_packed_kv_attention(ctypes.byref(a), None) == status
+    assert len(lib.sqg_last_error()) > 0
+
+
+def test_test_entry_argument_errors():
+    lib = sqg.load()
+    assert lib.sqg_test_quant_pack_f32(FAKE, 10, 3, FAKE, FAKE, None) == -1
+    assert lib.sqg_test_quant_pack_f32(FAKE + 4, 10, 0, FAKE, FAKE, None) == -3
+    assert lib.sqg_test_quant_pack_f32(FAKE, 0, 0, None, None, None) == 0
+    assert lib.sqg_test_fwht_f32(FAKE, FAKE, -1, 0, None) == -1
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((256, 256), dtype=torch.bfloat16)
+    w = torch.zeros((256, 768), dtype=torch.bfloat16)
+    with pytest.raises((ValueError, RuntimeError)):
+        sqg.streamed_qkv_quant(x, w, out={"q": x, "kpack": x, "vpack": x, "kscale": x, "vscale": x})

@@ -1,0 +1,79 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (same chunking, same KV blocking), checked on sampled rows that the
+oracle computes one by one: G2 on sampled token rows (including every chunk and
+range boundary), G3 on sampled query rows of a few heads against all keys."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+DEV = "cuda"
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def build_inputs(wl):
+    x = synth.make_x(wl.n_tokens, wl.d_model, wl.outlier_frac, seed=wl.seed_base + 1, device=DEV,
+                     outlier_seed=wl.seed_base + 3)
+    w = synth.make_w(wl.d_model, seed=wl.seed_base + 2, device=DEV)
+    norm = synth.make_norm_weights(wl.seed_base + 4) if wl.norm_rope else None
+    return x, w, norm
+
+
+@pytest.mark.parametrize("name", ["h3_16k", "h3_64k_mixed", "h3_152k_odd", "h3_217k_normrope"])
+def test_fullsize_parity(lib, name):
+    wl = synth.WORKLOADS[name]
+    N, d, H = wl.n_tokens, wl.d_model, wl.n_heads
+    print("[fullsize] %s N=%d d=%d" % (name, N, d), flush=True)
+    x, w, norm = build_inputs(wl)
+    kw = {}
+    if wl.norm_rope:
+        kw["q_norm_w"], kw["k_norm_w"] = norm[0].to(DEV), norm[1].to(DEV)
+        kw["rope_cos"], kw["rope_sin"] = lib.rope_table(N, 10000.0, device=DEV)
+    ranges = wl.ranges
+    store = lib.streamed_qkv_quant(x, w, ranges=ranges, chunk_rows=wl.chunk_rows, **kw)
+    o, lse = lib.packed_kv_attention(store, kv_block=wl.kv_block)
+    torch.cuda.synchronize()
+
+    # ---- G2 on sampled token rows
+    extra = [b for (b, _, _) in wl.range_list()[1:]]
+    must = synth.boundary_rows(N, wl.chunk_rows, extra)
+    rows = synth.sample_rows(N, 48, seed=wl.seed_base + 5, must=must).numpy()
+    segs = oracle.range_segments(N, ranges)
+    fm = oracle.token_formats(N, segs)[rows]
+    xb = synth.bf16_bits(x[torch.from_numpy(rows).to(DEV)])
+    okw = {}
+    if wl.norm_rope:
+        okw = dict(q_norm_w=norm[0].numpy(), k_norm_w=norm[1].numpy(), eps=1e-6, rope_theta=10000.0)
+    ref = oracle.qkv_quant_rows(xb, synth.bf16_bits(w), H, rows, fm, **okw)
+    layout, _ = oracle.packed_layout(N, H, segs)
+    kp, vp = host(store["kpack"]), host(store["vpack"])
+    ks, vs = host(store["kscale"]), host(store["vscale"])
+    kc, _ = oracle.gather_packed_rows(kp, ks, layout, H, rows)
+    vc, _ = oracle.gather_packed_rows(vp, vs, layout, H, rows)
+    qb = synth.bf16_bits(store["q"])
+    for got, want in ((kc, ref["k_codes"]), (vc, ref["v_codes"])):
+        dd = np.abs(got.astype(np.int64) - want.astype(np.int64))
+        assert dd.max() <= 1 and np.mean(dd == 0) >= 0.999, (name, dd.max(), np.mean(dd == 0))
+    qd = np.abs(qb[rows].astype(np.int64) - ref["q_bits"].astype(np.int64))
+    assert qd.max() <= 1 and np.mean(qd == 0) >= 0.99
+
+    # ---- G3 on sampled query rows of a few heads, all keys
+    qrows = synth.sample_rows(N, 12, seed=wl.seed_base + 6, must=[N - 1]).numpy()
+    heads = [0, H // 2, H - 1]
+    o_ref, lse_ref = oracle.attention_rows_from_store(qb[qrows], qrows, kp, vp, ks, vs, layout, H, N,
+                                                      kv_block=wl.kv_block, heads=heads)
+    og = host(o)[qrows]
+    lg = host(lse)[:, qrows]
+    for h in heads:
+        sl = slice(128 * h, 128 * h + 128)
+        err = np.abs(og[:, sl] - o_ref[:, sl])
+        rel = np.linalg.norm(og[:, sl] - o_ref[:, sl]) / np.linalg.norm(o_ref[:, sl])
+        assert err.max() <= 2e-2 and rel <= 5e-3, (name, h, err.max(), rel)
+        assert np.max(np.abs(lg[h] - lse_ref[h])) <= 2e-3
