@@ -16,7 +16,7 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
-    "HEAD_DIM", "GROUP", "INT4", "INT8", "QMAX", "ROW_BYTES",
+    "HEAD_DIM", "GROUP", "INT4", "INT8", "QMAX", "ROW_BYTES", "SCALE_BITS", "round_up_bits",
     "hadamard_pm1", "rotation_matrix",
     "f32_to_bf16_bits", "bf16_bits_to_f64", "f32_to_f16",
     "chunk_ranges", "range_segments", "token_formats",
@@ -35,6 +35,9 @@ INT4 = 0                # token-range formats ([FR] "Mixed precision for conditi
 INT8 = 1
 QMAX = {INT4: 7, INT8: 127}
 ROW_BYTES = {INT4: HEAD_DIM // 2, INT8: HEAD_DIM}
+# significant bits kept in a group scale: code bits + scale bits <= 11, so code * scale
+# is exact in fp16 (INT4 codes need 3 bits, INT8 codes 7)
+SCALE_BITS = {INT4: 8, INT8: 4}
 
 
 # --------------------------------------------------------------------------- rotation
@@ -192,20 +195,36 @@ def rotate(u: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------- quantise / pack
+def round_up_bits(t: np.ndarray, bits: int) -> np.ndarray:
+    """Smallest fp32 value with at most `bits` significant bits that is >= t (t >= 0),
+    found on the bit pattern: clear the low 24 - bits significand bits, carrying up
+    when any of them was set."""
+    u = np.ascontiguousarray(np.asarray(t, dtype=np.float32)).view(np.uint32).astype(np.uint64)
+    mask = (1 << (24 - bits)) - 1
+    u = np.where(u & mask, (u | mask) + 1, u)
+    return u.astype(np.uint32).view(np.float32)
+
+
 def quantize_groups(r: np.ndarray, qmax: int):
     """Group quantisation of fp32 rotated vectors [..., 128] in groups of 32.
 
-    For each group: a = max |r| (fp32); s = fp16_RNE(a / qmax) with the division
-    in IEEE fp32; if s == 0 every code is 0; otherwise c = clamp(rne(r / fp32(s)),
-    -qmax, qmax) with round-half-to-even and IEEE fp32 division.
+    For each group: a = max |r| (fp32); t = a / qmax in IEEE fp32; the scale s is t
+    rounded UP to SCALE_BITS significant bits, stored as fp16; if s == 0 every code
+    is 0; otherwise c = clamp(rne(r / fp32(s)), -qmax, qmax) with
+    round-half-to-even and IEEE fp32 division.
     [VL] precision-probe section, `_fq_int4` (absmax / 7, round, clamp) and kvi8r
-    `_Int8KV.store` (absmax / 127, round, clamp to +-127); the workloads give
-    group 32 along head_dim and fp16 scales.  Returns (codes int8, scales fp16)."""
+    `_Int8KV.store` (absmax / 127 with the scale rounded UP so codes stay within
+    +-127); the workloads give group 32 along head_dim and fp16 scales.  Reading:
+    the scale keeps few enough bits that code * scale is exact in fp16 (8 bits for
+    INT4, 4 for INT8, rounded up as the page rounds its int8 scale up).
+    Returns (codes int8, scales fp16)."""
     r = np.ascontiguousarray(np.asarray(r, dtype=np.float32))
     lead = r.shape[:-1]
     g = r.reshape(lead + (HEAD_DIM // GROUP, GROUP))
     a = np.max(np.abs(g), axis=-1)                                  # fp32, exact
-    s16 = (a / np.float32(qmax)).astype(np.float32).astype(np.float16)
+    bits = 8 if qmax == QMAX[INT4] else 4
+    t = (a / np.float32(qmax)).astype(np.float32)
+    s16 = round_up_bits(t, bits).astype(np.float16)
     s32 = s16.astype(np.float32)
     safe = np.where(s32 == 0, np.float32(1), s32)
     q = np.rint(g / safe[..., None])                                # fp32 division, RNE

@@ -10,9 +10,13 @@
 // online softmax, and the output is rotated back once.  That page also measured
 // that the rotated basis needs fp16 operands rather than bf16 (rotation spreads
 // every value to the same magnitude), so both products use f16 MFMA with fp32
-// accumulation.
+// accumulation.  Two further steps keep the scores accurate where softmax is
+// sharp: K/V dequantise exactly (the store's scales carry few enough bits that
+// code * scale is an fp16 value), and the rotated query is split into an f16 high
+// part and an f16 remainder, so S = K (q_hi + q_lo) costs two MFMAs per step and
+// carries ~22 bits of the query.
 //
-// Workgroup: 256 queries of one head, four waves of 64 queries.  Per 64-key tile
+// Workgroup: 256 queries of one head, four waves of 64 queries.  Per 32-key tile
 // the workgroup loads the packed codes and fp16 scales once, dequantises them to
 // f16 in LDS (K row-major, V transposed), and every wave computes
 //   S^T = K_r Q_r^T        (keys x queries, 32x32x16 f16 MFMA)
@@ -28,13 +32,14 @@ namespace sqg {
 namespace {
 
 constexpr int kBQ = 256;              // queries per workgroup
-constexpr int kBKV = 64;              // keys per tile
+constexpr int kBKV = 32;              // keys per tile
 constexpr int kKStride = 128 + 8;     // f16 per K row in LDS (272 B)
-constexpr int kVStride = kBKV + 8;    // f16 per transposed V row in LDS (144 B)
+constexpr int kVStride = kBKV + 8;    // f16 per transposed V row in LDS (80 B)
 constexpr int kKTile = kBKV * kKStride;
+constexpr int kKB = kBKV / 32;         // 32-key MFMA blocks per tile
 constexpr int kVTile = 128 * kVStride;
 
-// position of key k (0..63) inside a transposed V row: bits 2 and 3 are swapped so
+// position of key k (0..31) inside a transposed V row: bits 2 and 3 are swapped so
 // that the 8 keys one lane feeds to a 16-key MFMA step are contiguous
 __device__ __forceinline__ int vpos(int k) {
   return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
@@ -53,7 +58,7 @@ __device__ __forceinline__ void dequant_int4x8(uint32_t w, uint32_t s2, uint32_t
     const uint32_t sel = (uint32_t)p | 0x0c00u | ((uint32_t)(4 + p) << 16) | 0x0c000000u;
     const uint32_t pr = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
     f16x2 v = __builtin_bit_cast(f16x2, pr) + bias;  // exact code
-    v = v * sc;                                       // one rounding to f16
+    v = v * sc;                                       // exact: the scale has few bits
     out[p] = __builtin_bit_cast(uint32_t, v);
   }
 }
@@ -74,9 +79,9 @@ __device__ __forceinline__ void dequant_int8x4(uint32_t w, uint32_t s2, uint32_t
 }
 
 struct TileRegs {
-  u32x4 k[2];      // K codes of one (key, group): 16 B INT4 or 32 B INT8
-  uint32_t kscale; // fp16 scale of that group
-  u32x2 v[4];      // V codes of 4 keys x 8 dims: 4 B INT4 or 8 B INT8 each
+  u32x4 k;          // K codes of (key, 16 dims): 8 B INT4 (k[0..1]) or 16 B INT8
+  uint32_t kscale;  // fp16 scale of that group
+  uint32_t v[4];    // V codes of 4 keys x 4 dims: 2 B INT4 or 4 B INT8 each
   uint32_t vscale[4];
   int fmt;
 };
@@ -93,9 +98,9 @@ __global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnPara
   const int head = blockIdx.y;
   const int64_t N = p.n_tokens;
 
-  // ---- query tile: rotate once, keep as f16 MFMA B operands
+  // ---- query tile: rotate once, keep as f16 MFMA B operands (high part + remainder)
   const int64_t qw0 = p.q_begin + (int64_t)blockIdx.x * kBQ + 64 * wave;
-  f16x8 qf[2][8];
+  f16x8 qf[2][8], ql[2][8];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int64_t row = qw0 + 32 * qb + l32;
@@ -141,16 +146,18 @@ __global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnPara
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float pr = xor32(v[ks][j]);
-        const float r = hsel ? (pr - v[ks][j]) : (v[ks][j] + pr);
-        qf[qb][ks][j] = (_Float16)(r * kInvSqrtHeadDim);
+        const float r = (hsel ? (pr - v[ks][j]) : (v[ks][j] + pr)) * kInvSqrtHeadDim;
+        const _Float16 hi = (_Float16)r;
+        qf[qb][ks][j] = hi;
+        ql[qb][ks][j] = (_Float16)(r - (float)hi);
       }
   }
 
-  // ---- per-thread maps for the K/V tile loads
-  const int kkey = tid >> 2;   // K: key of the tile, group (tid & 3)
-  const int kgrp = tid & 3;
-  const int vq = tid & 15;     // V: keys 4 vq .. 4 vq + 3, dims 8 vd .. 8 vd + 7
-  const int vd = tid >> 4;
+  // ---- per-thread maps for the K/V tile loads (32 keys per tile, 256 threads)
+  const int kkey = tid >> 3;   // K: key of the tile, dims 16 kpart .. + 15
+  const int kpart = tid & 7;
+  const int vq = tid & 7;      // V: keys 4 vq .. 4 vq + 3, dims 4 vd .. 4 vd + 3
+  const int vd = tid >> 3;
 
   auto load_tile = [&](int64_t key0, TileRegs& r) {
     const int seg = find_segment(p.seg, key0);
@@ -164,38 +171,33 @@ __global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnPara
     const uint8_t* vb = p.vpack + p.seg.offset[seg];
     {
       const int64_t key = key0 + kkey;
-      const bool ok = key < p.kv_end;
-      const int64_t kk = ok ? key : key0;
-      const uint8_t* src = kb + (hrow + kk) * rb;
       u32x4 z = {0u, 0u, 0u, 0u};
-      r.k[0] = z;
-      r.k[1] = z;
+      r.k = z;
       r.kscale = 0u;
-      if (ok) {
+      if (key < p.kv_end) {
+        const uint8_t* src = kb + (hrow + key) * rb;
         if (fmt == FMT_INT4) {
-          r.k[0] = *reinterpret_cast<const u32x4*>(src + 16 * kgrp);
+          const u32x2 c = *reinterpret_cast<const u32x2*>(src + 8 * kpart);
+          r.k[0] = c[0];
+          r.k[1] = c[1];
         } else {
-          r.k[0] = *reinterpret_cast<const u32x4*>(src + 32 * kgrp);
-          r.k[1] = *reinterpret_cast<const u32x4*>(src + 32 * kgrp + 16);
+          r.k = *reinterpret_cast<const u32x4*>(src + 16 * kpart);
         }
-        r.kscale = p.kscale[((int64_t)head * N + key) * 4 + kgrp];
+        r.kscale = p.kscale[((int64_t)head * N + key) * 4 + (kpart >> 1)];
       }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t key = key0 + 4 * vq + j;
-      const bool ok = key < p.kv_end;
-      u32x2 z = {0u, 0u};
-      r.v[j] = z;
+      r.v[j] = 0u;
       r.vscale[j] = 0u;
-      if (ok) {
+      if (key < p.kv_end) {
         const uint8_t* src = vb + (hrow + key) * rb;
-        if (fmt == FMT_INT4) {
-          r.v[j][0] = *reinterpret_cast<const uint32_t*>(src + 4 * vd);
-        } else {
-          r.v[j] = *reinterpret_cast<const u32x2*>(src + 8 * vd);
-        }
-        r.vscale[j] = p.vscale[((int64_t)head * N + key) * 4 + (vd >> 2)];
+        if (fmt == FMT_INT4)
+          r.v[j] = *reinterpret_cast<const uint16_t*>(src + 2 * vd);
+        else
+          r.v[j] = *reinterpret_cast<const uint32_t*>(src + 4 * vd);
+        r.vscale[j] = p.vscale[((int64_t)head * N + key) * 4 + (vd >> 3)];
       }
     }
   };
@@ -204,50 +206,53 @@ __global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnPara
     _Float16* K = sK[stage];
     _Float16* V = sV[stage];
     const uint32_t ks2 = r.kscale | (r.kscale << 16);
-    // K: 32 values of (key, group) -> row kkey, elements 32 kgrp ..
+    // K: 16 values of (key, part) -> row kkey, elements 16 kpart ..
+    uint32_t o[8];
     if (r.fmt == FMT_INT4) {
+      uint32_t a[4], b[4];
+      dequant_int4x8(r.k[0], ks2, a);
+      dequant_int4x8(r.k[1], ks2, b);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t o[4];
-        dequant_int4x8(r.k[0][w], ks2, o);
-        u32x4 ov = {o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<u32x4*>(K + kkey * kKStride + 32 * kgrp + 8 * w) = ov;
-      }
+      for (int i = 0; i < 4; ++i) { o[i] = a[i]; o[4 + i] = b[i]; }
     } else {
 #pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        uint32_t o[2];
-        dequant_int8x4(r.k[w >> 2][w & 3], ks2, o);
-        u32x2 ov = {o[0], o[1]};
-        *reinterpret_cast<u32x2*>(K + kkey * kKStride + 32 * kgrp + 4 * w) = ov;
+      for (int w = 0; w < 4; ++w) {
+        uint32_t c[2];
+        dequant_int8x4(r.k[w], ks2, c);
+        o[2 * w] = c[0];
+        o[2 * w + 1] = c[1];
       }
     }
-    // V: 4 keys x 8 dims, written transposed: row = dim, 4 keys contiguous
-    _Float16 vals[4][8];
+    u32x4 o0 = {o[0], o[1], o[2], o[3]};
+    u32x4 o1 = {o[4], o[5], o[6], o[7]};
+    *reinterpret_cast<u32x4*>(K + kkey * kKStride + 16 * kpart) = o0;
+    *reinterpret_cast<u32x4*>(K + kkey * kKStride + 16 * kpart + 8) = o1;
+    // V: 4 keys x 4 dims, written transposed: row = dim, the 4 keys contiguous
+    _Float16 vals[4][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t s2 = r.vscale[j] | (r.vscale[j] << 16);
-      uint32_t o[4];
+      uint32_t c[4];
       if (r.fmt == FMT_INT4) {
-        dequant_int4x8(r.v[j][0], s2, o);
+        dequant_int4x8(r.v[j], s2, c);   // codes 0..3 sit in the low 16 bits
       } else {
-        uint32_t a[2], b[2];
-        dequant_int8x4(r.v[j][0], s2, a);
-        dequant_int8x4(r.v[j][1], s2, b);
-        o[0] = a[0]; o[1] = a[1]; o[2] = b[0]; o[3] = b[1];
+        uint32_t c8[2];
+        dequant_int8x4(r.v[j], s2, c8);
+        c[0] = c8[0];
+        c[1] = c8[1];
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const f16x2 h2 = __builtin_bit_cast(f16x2, o[e]);
+      for (int e = 0; e < 2; ++e) {
+        const f16x2 h2 = __builtin_bit_cast(f16x2, c[e]);
         vals[j][2 * e] = h2[0];
         vals[j][2 * e + 1] = h2[1];
       }
     }
     const int pos = vpos(4 * vq);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 4; ++e) {
       f16x4 col = {vals[0][e], vals[1][e], vals[2][e], vals[3][e]};
-      *reinterpret_cast<f16x4*>(V + (8 * vd + e) * kVStride + pos) = col;
+      *reinterpret_cast<f16x4*>(V + (4 * vd + e) * kVStride + pos) = col;
     }
   };
 
@@ -275,10 +280,10 @@ __global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnPara
     const int64_t key0 = kv0 + (int64_t)it * kBKV;
     if (it + 1 < n_tiles) load_tile(key0 + kBKV, regs);
 
-    // S^T = K Q^T for 64 keys x 64 queries of this wave
-    f32x16 s[2][2];
+    // S^T = K (q_hi + q_lo)^T for the tile's keys x this wave's 64 queries
+    f32x16 s[kKB][2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < kKB; ++a)
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -287,19 +292,21 @@ __global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnPara
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < kKB; ++kb) {
         const f16x8 kf =
             *reinterpret_cast<const f16x8*>(K + (32 * kb + l32) * kKStride + 16 * ks + 8 * hsel);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < 2; ++qb) {
           s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[qb][ks], s[kb][qb], 0, 0, 0);
+          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, ql[qb][ks], s[kb][qb], 0, 0, 0);
+        }
       }
     }
 
     // mask keys past the end (last tile only)
     if (key0 + kBKV > p.kv_end) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int64_t key = key0 + 32 * kb + 8 * (e >> 2) + 4 * hsel + (e & 3);
@@ -311,12 +318,12 @@ __global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnPara
     }
 
     // online softmax down each query column; P^T as f16 B operands
-    f16x8 pf[2][4];
+    f16x8 pf[2][2 * kKB];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][qb][e]);
       mx = fmaxf(mx, xor32(mx));
@@ -325,7 +332,7 @@ __global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnPara
       m_run[qb] = m_new;
       float lsum = 0.0f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const float pv = exp2f(s[kb][qb][e] * c - m_new);
@@ -342,7 +349,7 @@ __global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnPara
     // O^T += V^T P^T
     const _Float16* V = sV[stage];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 2 * kKB; ++ks) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const f16x8 vf =

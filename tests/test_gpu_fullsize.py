@@ -8,6 +8,7 @@ import torch
 
 import oracle
 import synth
+from test_gpu_parity import q_gate
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -61,8 +62,7 @@ def test_fullsize_parity(lib, name):
     for got, want in ((kc, ref["k_codes"]), (vc, ref["v_codes"])):
         dd = np.abs(got.astype(np.int64) - want.astype(np.int64))
         assert dd.max() <= 1 and np.mean(dd == 0) >= 0.999, (name, dd.max(), np.mean(dd == 0))
-    qd = np.abs(qb[rows].astype(np.int64) - ref["q_bits"].astype(np.int64))
-    assert qd.max() <= 1 and np.mean(qd == 0) >= 0.99
+    q_gate(qb[rows], ref["q_bits"], name)
 
     # ---- G3 on sampled query rows of a few heads, all keys
     qrows = synth.sample_rows(N, 12, seed=wl.seed_base + 6, must=[N - 1]).numpy()

