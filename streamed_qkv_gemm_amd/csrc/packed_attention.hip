@@ -16,31 +16,38 @@
 // part and an f16 remainder, so S = K (q_hi + q_lo) costs two MFMAs per step and
 // carries ~22 bits of the query.
 //
-// Workgroup: 256 queries of one head, four waves of 64 queries.  Per 32-key tile
-// the workgroup loads the packed codes and fp16 scales once, dequantises them to
-// f16 in LDS (K row-major, V transposed), and every wave computes
+// Workgroup: 256 queries of one head, eight waves of 32 queries (two waves per
+// SIMD, so one wave's softmax and dequantisation overlap the other's MFMAs).
+// Per 64-key tile the workgroup loads the packed codes and fp16 scales once,
+// dequantises them to f16 in LDS (K row-major, V transposed), and every wave
+// computes
 //   S^T = K_r Q_r^T        (keys x queries, 32x32x16 f16 MFMA)
 //   online softmax down each query column (one lane-pair exchange per tile)
 //   O^T += V_r^T P^T       (dims x queries)
 // The transposed products keep a query's scores and its 128 output values in one
 // lane pair, so the softmax statistics and the final inverse rotation are
-// register-local apart from one exchange with lane ^ 32.
+// register-local apart from one exchange with lane ^ 32.  The running maximum is
+// only moved (and O rescaled) when a column's maximum grows by more than 2^8, so
+// most tiles skip the rescale; P then stays below 256, well inside f16.
 #include "device_common.h"
 #include "internal.h"
 
 namespace sqg {
 namespace {
 
-constexpr int kBQ = 256;              // queries per workgroup
-constexpr int kBKV = 32;              // keys per tile
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBQ = 32 * kWaves;      // queries per workgroup
+constexpr int kBKV = 64;              // keys per tile
+constexpr int kKB = kBKV / 32;        // 32-key MFMA blocks per tile
 constexpr int kKStride = 128 + 8;     // f16 per K row in LDS (272 B)
-constexpr int kVStride = kBKV + 8;    // f16 per transposed V row in LDS (80 B)
+constexpr int kVStride = kBKV + 8;    // f16 per transposed V row in LDS (144 B)
 constexpr int kKTile = kBKV * kKStride;
-constexpr int kKB = kBKV / 32;         // 32-key MFMA blocks per tile
 constexpr int kVTile = 128 * kVStride;
+constexpr float kRescaleLog2 = 8.0f;  // move the running max only past this growth
 
-// position of key k (0..31) inside a transposed V row: bits 2 and 3 are swapped so
-// that the 8 keys one lane feeds to a 16-key MFMA step are contiguous
+// position of key k (0..kBKV-1) inside a transposed V row: bits 2 and 3 are swapped
+// so that the 8 keys one lane feeds to a 16-key MFMA step are contiguous
 __device__ __forceinline__ int vpos(int k) {
   return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
@@ -78,15 +85,18 @@ __device__ __forceinline__ void dequant_int8x4(uint32_t w, uint32_t s2, uint32_t
   }
 }
 
+// Packed codes and scales one thread moves per tile:
+//   K: one key, 16 dims (8 B INT4 in k[0..1], 16 B INT8 in k[0..3]) and its group scale;
+//   V: 4 keys x 4 dims (2 B INT4 or 4 B INT8 per key) and their scales.
 struct TileRegs {
-  u32x4 k;          // K codes of (key, 16 dims): 8 B INT4 (k[0..1]) or 16 B INT8
-  uint32_t kscale;  // fp16 scale of that group
-  uint32_t v[4];    // V codes of 4 keys x 4 dims: 2 B INT4 or 4 B INT8 each
+  u32x4 k;
+  uint32_t kscale;
+  uint32_t v[4];
   uint32_t vscale[4];
   int fmt;
 };
 
-__global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnParams p) {
+__global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(16))) _Float16 sK[2][kKTile];
   __shared__ __attribute__((aligned(16))) _Float16 sV[2][kVTile];
 
@@ -99,19 +109,17 @@ __global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnPara
   const int64_t N = p.n_tokens;
 
   // ---- query tile: rotate once, keep as f16 MFMA B operands (high part + remainder)
-  const int64_t qw0 = p.q_begin + (int64_t)blockIdx.x * kBQ + 64 * wave;
-  f16x8 qf[2][8], ql[2][8];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int64_t row = qw0 + 32 * qb + l32;
-    const bool valid = row < p.q_end;
-    const uint16_t* src = p.q + (valid ? row : 0) * p.ldq + head * kHeadDim + 8 * hsel;
+  const int64_t qrow = p.q_begin + (int64_t)blockIdx.x * kBQ + 32 * wave + l32;
+  const bool qvalid = qrow < p.q_end;
+  f16x8 qf[8], ql[8];
+  {
+    const uint16_t* src = p.q + (qvalid ? qrow : 0) * p.ldq + head * kHeadDim + 8 * hsel;
     // element e(ks, j) = 16 ks + 8 hsel + j: bits 0-2 = j, bit 3 = lane pair, bits 4-6 = ks
     float v[8][8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       u32x4 raw = {0u, 0u, 0u, 0u};
-      if (valid) raw = *reinterpret_cast<const u32x4*>(src + 16 * ks);
+      if (qvalid) raw = *reinterpret_cast<const u32x4*>(src + 16 * ks);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         v[ks][2 * j] = bf16_lo(raw[j]);
@@ -148,16 +156,16 @@ __global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnPara
         const float pr = xor32(v[ks][j]);
         const float r = (hsel ? (pr - v[ks][j]) : (v[ks][j] + pr)) * kInvSqrtHeadDim;
         const _Float16 hi = (_Float16)r;
-        qf[qb][ks][j] = hi;
-        ql[qb][ks][j] = (_Float16)(r - (float)hi);
+        qf[ks][j] = hi;
+        ql[ks][j] = (_Float16)(r - (float)hi);
       }
   }
 
-  // ---- per-thread maps for the K/V tile loads (32 keys per tile, 256 threads)
+  // ---- per-thread maps for the K/V tile loads (64 keys per tile, 512 threads)
   const int kkey = tid >> 3;   // K: key of the tile, dims 16 kpart .. + 15
   const int kpart = tid & 7;
-  const int vq = tid & 7;      // V: keys 4 vq .. 4 vq + 3, dims 4 vd .. 4 vd + 3
-  const int vd = tid >> 3;
+  const int vq = tid & 15;     // V: keys 4 vq .. 4 vq + 3, dims 4 vd .. 4 vd + 3
+  const int vd = tid >> 4;
 
   auto load_tile = [&](int64_t key0, TileRegs& r) {
     const int seg = find_segment(p.seg, key0);
@@ -177,9 +185,9 @@ __global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnPara
       if (key < p.kv_end) {
         const uint8_t* src = kb + (hrow + key) * rb;
         if (fmt == FMT_INT4) {
-          const u32x2 c = *reinterpret_cast<const u32x2*>(src + 8 * kpart);
-          r.k[0] = c[0];
-          r.k[1] = c[1];
+          const u32x2 cw = *reinterpret_cast<const u32x2*>(src + 8 * kpart);
+          r.k[0] = cw[0];
+          r.k[1] = cw[1];
         } else {
           r.k = *reinterpret_cast<const u32x4*>(src + 16 * kpart);
         }
@@ -213,14 +221,17 @@ __global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnPara
       dequant_int4x8(r.k[0], ks2, a);
       dequant_int4x8(r.k[1], ks2, b);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { o[i] = a[i]; o[4 + i] = b[i]; }
+      for (int i = 0; i < 4; ++i) {
+        o[i] = a[i];
+        o[4 + i] = b[i];
+      }
     } else {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        uint32_t c[2];
-        dequant_int8x4(r.k[w], ks2, c);
-        o[2 * w] = c[0];
-        o[2 * w + 1] = c[1];
+        uint32_t cw[2];
+        dequant_int8x4(r.k[w], ks2, cw);
+        o[2 * w] = cw[0];
+        o[2 * w + 1] = cw[1];
       }
     }
     u32x4 o0 = {o[0], o[1], o[2], o[3]};
@@ -232,18 +243,18 @@ __global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnPara
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t s2 = r.vscale[j] | (r.vscale[j] << 16);
-      uint32_t c[4];
+      uint32_t cw[4];
       if (r.fmt == FMT_INT4) {
-        dequant_int4x8(r.v[j], s2, c);   // codes 0..3 sit in the low 16 bits
+        dequant_int4x8(r.v[j], s2, cw);   // codes 0..3 sit in the low 16 bits
       } else {
         uint32_t c8[2];
         dequant_int8x4(r.v[j], s2, c8);
-        c[0] = c8[0];
-        c[1] = c8[1];
+        cw[0] = c8[0];
+        cw[1] = c8[1];
       }
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const f16x2 h2 = __builtin_bit_cast(f16x2, c[e]);
+        const f16x2 h2 = __builtin_bit_cast(f16x2, cw[e]);
         vals[j][2 * e] = h2[0];
         vals[j][2 * e + 1] = h2[1];
       }
@@ -257,16 +268,15 @@ __global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnPara
   };
 
   // ---- state
-  f32x16 oacc[4][2];
+  f32x16 oacc[4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[a][b][e] = 0.0f;
-  float m_run[2] = {-INFINITY, -INFINITY};  // running max of scale*log2e*score
-  float l_run[2] = {0.0f, 0.0f};            // lane-partial running sum
+    for (int e = 0; e < 16; ++e) oacc[a][e] = 0.0f;
+  float m_run = -INFINITY;  // reference max of scale*log2e*score for this query column
+  float l_run = 0.0f;       // lane-partial sum of the f16 P values
   const float c = p.scale_log2;
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
   const int64_t kv0 = p.kv_begin;
   const int n_tiles = (int)((p.kv_end - kv0 + kBKV - 1) / kBKV);
@@ -280,14 +290,12 @@ __global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnPara
     const int64_t key0 = kv0 + (int64_t)it * kBKV;
     if (it + 1 < n_tiles) load_tile(key0 + kBKV, regs);
 
-    // S^T = K (q_hi + q_lo)^T for the tile's keys x this wave's 64 queries
-    f32x16 s[kKB][2];
+    // S^T = K (q_hi + q_lo)^T for the tile's keys x this wave's 32 queries
+    f32x16 s[kKB];
 #pragma unroll
     for (int a = 0; a < kKB; ++a)
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[a][b][e] = 0.0f;
+      for (int e = 0; e < 16; ++e) s[a][e] = 0.0f;
     const _Float16* K = sK[stage];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
@@ -295,11 +303,8 @@ __global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnPara
       for (int kb = 0; kb < kKB; ++kb) {
         const f16x8 kf =
             *reinterpret_cast<const f16x8*>(K + (32 * kb + l32) * kKStride + 16 * ks + 8 * hsel);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[qb][ks], s[kb][qb], 0, 0, 0);
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, ql[qb][ks], s[kb][qb], 0, 0, 0);
-        }
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], s[kb], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, ql[ks], s[kb], 0, 0, 0);
       }
     }
 
@@ -310,41 +315,39 @@ __global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnPara
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int64_t key = key0 + 32 * kb + 8 * (e >> 2) + 4 * hsel + (e & 3);
-          if (key >= p.kv_end) {
-            s[kb][0][e] = -INFINITY;
-            s[kb][1][e] = -INFINITY;
-          }
+          if (key >= p.kv_end) s[kb][e] = -INFINITY;
         }
     }
 
-    // online softmax down each query column; P^T as f16 B operands
-    f16x8 pf[2][2 * kKB];
+    // online softmax down the query column; P^T as f16 B operands
+    float mx = -INFINITY;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mx = -INFINITY;
+    for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][qb][e]);
-      mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m_run[qb], mx * c);
-      const float alpha = exp2f(m_run[qb] - m_new);
-      m_run[qb] = m_new;
-      float lsum = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float pv = exp2f(s[kb][qb][e] * c - m_new);
-          lsum += pv;
-          pf[qb][2 * kb + (e >> 3)][e & 7] = (_Float16)pv;
-        }
-      l_run[qb] = l_run[qb] * alpha + lsum;
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
+    mx = fmaxf(mx, xor32(mx)) * c;
+    if (__any(mx > m_run + kRescaleLog2)) {  // wave-uniform: move every column's max
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[db][qb][e] *= alpha;
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
     }
+    f16x8 pf[2 * kKB];
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(s[kb][e] * c - m_run);
+        const float p1 = __builtin_amdgcn_exp2f(s[kb][e + 1] * c - m_run);
+        const f16x2 h2 = {(_Float16)p0, (_Float16)p1};
+        l_run = __builtin_amdgcn_fdot2(h2, ones, l_run, false);
+        pf[2 * kb + (e >> 3)][e & 7] = h2[0];
+        pf[2 * kb + (e >> 3)][(e & 7) + 1] = h2[1];
+      }
 
     // O^T += V^T P^T
     const _Float16* V = sV[stage];
@@ -354,9 +357,7 @@ __global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnPara
       for (int db = 0; db < 4; ++db) {
         const f16x8 vf =
             *reinterpret_cast<const f16x8*>(V + (32 * db + l32) * kVStride + 16 * ks + 8 * hsel);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[qb][ks], oacc[db][qb], 0, 0, 0);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[ks], oacc[db], 0, 0, 0);
       }
     }
 
@@ -365,73 +366,67 @@ __global__ __launch_bounds__(256, 1) void packed_attention_kernel(const AttnPara
   }
 
   // ---- epilogue: normalise, rotate back, merge, store
+  const float l_tot = l_run + xor32(l_run);
+  const float inv = 1.0f / l_tot;
+  float u[4][16];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int64_t row = qw0 + 32 * qb + l32;
-    const bool valid = row < p.q_end;
-    const float l_tot = l_run[qb] + xor32(l_run[qb]);
-    const float inv = 1.0f / l_tot;
-    float u[4][16];
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) u[db][e] = oacc[db][e] * inv;
+  fwht128_cols(u);
+  float lse = (m_run + log2f(l_tot)) * 0.6931471805599453f;
+  const int64_t rr = qvalid ? qrow : 0;
+  if (p.accumulate) {
+    const float* orow = reinterpret_cast<const float*>(p.o) + rr * p.ldo + head * kHeadDim + 4 * hsel;
+    const float lse_old = p.lse[(int64_t)head * N + rr];
+    const float mxl = fmaxf(lse_old, lse);
+    const float lse_new = mxl + logf(expf(lse_old - mxl) + expf(lse - mxl));
+    const float w_old = expf(lse_old - lse_new);
+    const float w_new = expf(lse - lse_new) * kInvSqrtHeadDim;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) u[db][e] = oacc[db][qb][e] * inv;
-    fwht128_cols(u);
-    float lse = (m_run[qb] + log2f(l_tot)) * 0.6931471805599453f;
-    const int64_t rr = valid ? row : 0;
-    if (p.accumulate) {
-      const float* orow = reinterpret_cast<const float*>(p.o) + rr * p.ldo + head * kHeadDim + 4 * hsel;
-      const float lse_old = p.lse[(int64_t)head * N + rr];
-      const float mx = fmaxf(lse_old, lse);
-      const float lse_new = mx + logf(expf(lse_old - mx) + expf(lse - mx));
-      const float w_old = expf(lse_old - lse_new);
-      const float w_new = expf(lse - lse_new) * kInvSqrtHeadDim;
+      for (int q = 0; q < 4; ++q) {
+        f32x4 prev = {0.f, 0.f, 0.f, 0.f};
+        if (qvalid) prev = *reinterpret_cast<const f32x4*>(orow + 32 * db + 8 * q);
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f32x4 prev = {0.f, 0.f, 0.f, 0.f};
-          if (valid) prev = *reinterpret_cast<const f32x4*>(orow + 32 * db + 8 * q);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) u[db][4 * q + j] = prev[j] * w_old + u[db][4 * q + j] * w_new;
-        }
-      lse = lse_new;
-    } else {
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) u[db][e] *= kInvSqrtHeadDim;
-    }
-    if (valid) {
-      if (p.o_dtype == 0) {
-        float* orow = reinterpret_cast<float*>(p.o) + row * p.ldo + head * kHeadDim + 4 * hsel;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            f32x4 v = {u[db][4 * q], u[db][4 * q + 1], u[db][4 * q + 2], u[db][4 * q + 3]};
-            *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * q) = v;
-          }
-      } else {
-        uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + row * p.ldo + head * kHeadDim + 4 * hsel;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            u32x2 v;
-            if (p.o_dtype == 1) {
-              v[0] = f32_to_bf16_bits(u[db][4 * q]) | (f32_to_bf16_bits(u[db][4 * q + 1]) << 16);
-              v[1] = f32_to_bf16_bits(u[db][4 * q + 2]) | (f32_to_bf16_bits(u[db][4 * q + 3]) << 16);
-            } else {
-              v[0] = f32_to_f16_bits(u[db][4 * q]) | (f32_to_f16_bits(u[db][4 * q + 1]) << 16);
-              v[1] = f32_to_f16_bits(u[db][4 * q + 2]) | (f32_to_f16_bits(u[db][4 * q + 3]) << 16);
-            }
-            *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * q) = v;
-          }
+        for (int j = 0; j < 4; ++j) u[db][4 * q + j] = prev[j] * w_old + u[db][4 * q + j] * w_new;
       }
-      if (p.lse && hsel == 0) p.lse[(int64_t)head * N + row] = lse;
-    }
+    lse = lse_new;
+  } else {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) u[db][e] *= kInvSqrtHeadDim;
   }
+  if (!qvalid) return;
+  if (p.o_dtype == 0) {
+    float* orow = reinterpret_cast<float*>(p.o) + qrow * p.ldo + head * kHeadDim + 4 * hsel;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 v = {u[db][4 * q], u[db][4 * q + 1], u[db][4 * q + 2], u[db][4 * q + 3]};
+        *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * q) = v;
+      }
+  } else {
+    uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + qrow * p.ldo + head * kHeadDim + 4 * hsel;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x2 v;
+        if (p.o_dtype == 1) {
+          v[0] = f32_to_bf16_bits(u[db][4 * q]) | (f32_to_bf16_bits(u[db][4 * q + 1]) << 16);
+          v[1] = f32_to_bf16_bits(u[db][4 * q + 2]) | (f32_to_bf16_bits(u[db][4 * q + 3]) << 16);
+        } else {
+          v[0] = f32_to_f16_bits(u[db][4 * q]) | (f32_to_f16_bits(u[db][4 * q + 1]) << 16);
+          v[1] = f32_to_f16_bits(u[db][4 * q + 2]) | (f32_to_f16_bits(u[db][4 * q + 3]) << 16);
+        }
+        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * q) = v;
+      }
+  }
+  if (p.lse && hsel == 0) p.lse[(int64_t)head * N + qrow] = lse;
 }
 
 }  // namespace
@@ -440,8 +435,8 @@ int launch_packed_attention(const AttnParams& p, void* stream) {
   const int64_t nq = p.q_end - p.q_begin;
   if (nq <= 0 || p.kv_end <= p.kv_begin) return 0;
   const int64_t tiles = (nq + kBQ - 1) / kBQ;
-  hipLaunchKernelGGL(packed_attention_kernel, dim3((unsigned)tiles, (unsigned)p.n_heads), dim3(256),
-                     0, (hipStream_t)stream, p);
+  hipLaunchKernelGGL(packed_attention_kernel, dim3((unsigned)tiles, (unsigned)p.n_heads),
+                     dim3(kThreads), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
 

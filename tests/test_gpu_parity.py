@@ -270,7 +270,7 @@ def test_g3_kv_blocks_merge(lib):
     attention_gate(host(o2), o_ref, "blocked O")
     # blocks round P to f16 against their own maxima: agreement to that precision
     assert torch.allclose(o1, o2, rtol=0, atol=2e-3)
-    assert torch.allclose(l1, l2, rtol=0, atol=1e-4)
+    assert torch.allclose(l1, l2, rtol=0, atol=1e-3)
 
 
 def test_accumulate_two_halves_equals_full(lib):
@@ -281,7 +281,7 @@ def test_accumulate_two_halves_equals_full(lib):
     lib.packed_kv_attention(store, kv_begin=512, accumulate=True, o=o, lse=l)
     torch.cuda.synchronize()
     assert torch.allclose(o, o_full, rtol=0, atol=2e-3)
-    assert torch.allclose(l, l_full, rtol=0, atol=1e-4)
+    assert torch.allclose(l, l_full, rtol=0, atol=1e-3)
     rows = np.arange(0, N, 7)
     o_ref, lse_ref = oracle_attention(store, layout, H, rows)
     attention_gate(host(o)[rows], o_ref, "accumulated O")
