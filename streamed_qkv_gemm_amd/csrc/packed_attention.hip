@@ -45,6 +45,7 @@ constexpr int kVStride = kBKV + 8;    // f16 per transposed V row in LDS (144 B)
 constexpr int kKTile = kBKV * kKStride;
 constexpr int kVTile = 128 * kVStride;
 constexpr float kRescaleLog2 = 8.0f;  // move the running max only past this growth
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor, 32-bit data format
 
 // position of key k (0..kBKV-1) inside a transposed V row: bits 2 and 3 are swapped
 // so that the 8 keys one lane feeds to a 16-key MFMA step are contiguous
@@ -167,46 +168,51 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
   const int vq = tid & 15;     // V: keys 4 vq .. 4 vq + 3, dims 4 vd .. 4 vd + 3
   const int vd = tid >> 4;
 
+  // per-thread byte offsets inside a tile (same for every tile of a format)
+  const uint32_t k_off4 = (uint32_t)(kkey * 64 + 8 * kpart);
+  const uint32_t k_off8 = (uint32_t)(kkey * 128 + 16 * kpart);
+  const uint32_t ks_off = (uint32_t)(2 * (kkey * 4 + (kpart >> 1)));
+  const uint32_t v_off4 = (uint32_t)(4 * vq * 64 + 2 * vd);
+  const uint32_t v_off8 = (uint32_t)(4 * vq * 128 + 4 * vd);
+  const uint32_t vs_off = (uint32_t)(2 * (4 * vq * 4 + (vd >> 3)));
+
+  // Tile loads go through buffer resources whose base is the tile's first key
+  // (wave-uniform, scalar registers) and whose size ends at the head's last row of
+  // the segment: each thread adds a constant offset, and rows past the end of the
+  // segment (the ragged tail of the sequence) read as zero.
   auto load_tile = [&](int64_t key0, TileRegs& r) {
     const int seg = find_segment(p.seg, key0);
     const int fmt = p.seg.fmt[seg];
     const int64_t sb = p.seg.begin[seg];
-    const int64_t slen = p.seg.end[seg] - sb;
-    const int64_t hrow = (int64_t)head * slen - sb;
-    r.fmt = fmt;
+    const int64_t se = p.seg.end[seg];
     const int rb = fmt == FMT_INT4 ? 64 : 128;
-    const uint8_t* kb = p.kpack + p.seg.offset[seg];
-    const uint8_t* vb = p.vpack + p.seg.offset[seg];
-    {
-      const int64_t key = key0 + kkey;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      r.k = z;
-      r.kscale = 0u;
-      if (key < p.kv_end) {
-        const uint8_t* src = kb + (hrow + key) * rb;
-        if (fmt == FMT_INT4) {
-          const u32x2 cw = *reinterpret_cast<const u32x2*>(src + 8 * kpart);
-          r.k[0] = cw[0];
-          r.k[1] = cw[1];
-        } else {
-          r.k = *reinterpret_cast<const u32x4*>(src + 16 * kpart);
-        }
-        r.kscale = p.kscale[((int64_t)head * N + key) * 4 + (kpart >> 1)];
-      }
-    }
+    const int64_t row0 = (int64_t)head * (se - sb) + (key0 - sb);   // first key's row
+    const int32_t code_bytes = (int32_t)((se - key0) * rb);
+    const int32_t scale_bytes = (int32_t)((N - key0) * 8);
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.kpack + p.seg.offset[seg] + row0 * rb), 0, code_bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.vpack + p.seg.offset[seg] + row0 * rb), 0, code_bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.kscale + ((int64_t)head * N + key0) * 4), 0, scale_bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t vsr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.vscale + ((int64_t)head * N + key0) * 4), 0, scale_bytes, kBufferWord3);
+    r.fmt = fmt;
+    r.kscale = __builtin_amdgcn_raw_buffer_load_b16(ksr, ks_off, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t key = key0 + 4 * vq + j;
-      r.v[j] = 0u;
-      r.vscale[j] = 0u;
-      if (key < p.kv_end) {
-        const uint8_t* src = vb + (hrow + key) * rb;
-        if (fmt == FMT_INT4)
-          r.v[j] = *reinterpret_cast<const uint16_t*>(src + 2 * vd);
-        else
-          r.v[j] = *reinterpret_cast<const uint32_t*>(src + 4 * vd);
-        r.vscale[j] = p.vscale[((int64_t)head * N + key) * 4 + (vd >> 3)];
-      }
+    for (int j = 0; j < 4; ++j) r.vscale[j] = __builtin_amdgcn_raw_buffer_load_b16(vsr, vs_off + 8 * j, 0, 0);
+    if (fmt == FMT_INT4) {
+      const u32x2 cw = __builtin_amdgcn_raw_buffer_load_b64(kr, k_off4, 0, 0);
+      r.k[0] = cw[0];
+      r.k[1] = cw[1];
+      r.k[2] = 0u;
+      r.k[3] = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r.v[j] = __builtin_amdgcn_raw_buffer_load_b16(vr, v_off4 + 64 * j, 0, 0);
+    } else {
+      r.k = __builtin_amdgcn_raw_buffer_load_b128(kr, k_off8, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r.v[j] = __builtin_amdgcn_raw_buffer_load_b32(vr, v_off8 + 128 * j, 0, 0);
     }
   };
 
@@ -283,15 +289,19 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
   TileRegs regs;
   load_tile(kv0, regs);
   store_tile(regs, 0);
+  if (n_tiles > 1) load_tile(kv0 + kBKV, regs);
   __syncthreads();
 
-  for (int it = 0; it < n_tiles; ++it) {
-    const int stage = it & 1;
-    const int64_t key0 = kv0 + (int64_t)it * kBKV;
-    if (it + 1 < n_tiles) load_tile(key0 + kBKV, regs);
+  // Waves 0-3 and 4-7 share the four SIMDs (one of each per SIMD).  Between two
+  // barriers both run the same four steps, rotated by one for the second group so
+  // that on a SIMD one wave's MFMA step meets the other's VALU step:
+  //   waves 0-3: QK(j)    SM(j)    PV(j)    DQ(j+1)
+  //   waves 4-7: DQ(j+1)  QK(j)    SM(j)    PV(j)
+  // (QK = scores, SM = softmax, PV = output update, DQ = dequantise the next tile
+  // into the other LDS stage and start loading the one after.)
+  const bool lead = wave < kWaves / 2;
 
-    // S^T = K (q_hi + q_lo)^T for the tile's keys x this wave's 32 queries
-    f32x16 s[kKB];
+  auto do_qk = [&](int stage, f32x16 (&s)[kKB]) {
 #pragma unroll
     for (int a = 0; a < kKB; ++a)
 #pragma unroll
@@ -307,8 +317,9 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, ql[ks], s[kb], 0, 0, 0);
       }
     }
+  };
 
-    // mask keys past the end (last tile only)
+  auto do_softmax = [&](int64_t key0, f32x16 (&s)[kKB], f16x8 (&pf)[2 * kKB]) {
     if (key0 + kBKV > p.kv_end) {
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb)
@@ -318,8 +329,6 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
           if (key >= p.kv_end) s[kb][e] = -INFINITY;
         }
     }
-
-    // online softmax down the query column; P^T as f16 B operands
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
@@ -336,7 +345,6 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
     }
-    f16x8 pf[2 * kKB];
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
@@ -348,8 +356,9 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
         pf[2 * kb + (e >> 3)][e & 7] = h2[0];
         pf[2 * kb + (e >> 3)][(e & 7) + 1] = h2[1];
       }
+  };
 
-    // O^T += V^T P^T
+  auto do_pv = [&](int stage, const f16x8 (&pf)[2 * kKB]) {
     const _Float16* V = sV[stage];
 #pragma unroll
     for (int ks = 0; ks < 2 * kKB; ++ks) {
@@ -360,8 +369,23 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[ks], oacc[db], 0, 0, 0);
       }
     }
+  };
 
-    if (it + 1 < n_tiles) store_tile(regs, stage ^ 1);
+  auto do_dq = [&](int it) {   // dequantise tile it + 1, then start loading tile it + 2
+    if (it + 1 < n_tiles) store_tile(regs, (it + 1) & 1);
+    if (it + 2 < n_tiles) load_tile(kv0 + (int64_t)(it + 2) * kBKV, regs);
+  };
+
+  for (int it = 0; it < n_tiles; ++it) {
+    const int stage = it & 1;
+    const int64_t key0 = kv0 + (int64_t)it * kBKV;
+    if (!lead) do_dq(it);
+    f32x16 s[kKB];
+    f16x8 pf[2 * kKB];
+    do_qk(stage, s);
+    do_softmax(key0, s, pf);
+    do_pv(stage, pf);
+    if (lead) do_dq(it);
     __syncthreads();
   }
 
