@@ -31,6 +31,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kHeadDim = 128;
 constexpr int kGroup = 32;
+// word 3 of a raw buffer resource descriptor on gfx9-family GPUs (32-bit data format)
+constexpr int kBufferWord3 = 0x00020000;
 // 1/sqrt(128) rounded to fp32
 constexpr float kInvSqrtHeadDim = 0.0883883461356163f;
 

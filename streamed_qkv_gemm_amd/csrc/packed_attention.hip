@@ -45,7 +45,6 @@ constexpr int kVStride = kBKV + 8;    // f16 per transposed V row in LDS (144 B)
 constexpr int kKTile = kBKV * kKStride;
 constexpr int kVTile = 128 * kVStride;
 constexpr float kRescaleLog2 = 8.0f;  // move the running max only past this growth
-constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor, 32-bit data format
 
 // position of key k (0..kBKV-1) inside a transposed V row: bits 2 and 3 are swapped
 // so that the 8 keys one lane feeds to a 16-key MFMA step are contiguous

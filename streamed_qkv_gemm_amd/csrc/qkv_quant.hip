@@ -13,7 +13,10 @@
 // store; kvi8r section: rotated store.)
 //
 // Workgroup tile: 256 output columns (2 heads) x 256 tokens, K-step 64, four
-// waves in a 2 x 2 grid, each wave owning one head x 128 tokens.  The transposed
+// waves in a 2 x 2 grid, each wave owning one head x 128 tokens.  Slices of x and
+// W are fetched with range-checked buffer loads two K-steps ahead of their LDS
+// store (two register sets), LDS is double-buffered, and scheduling groups thread
+// the next step's operand reads between each step's MFMAs.  The transposed
 // product puts one token per lane column of each 32x32 MFMA block, so the head's
 // 128 values of a token sit in one lane pair: the Hadamard, the RMSNorm sum and the
 // group absmax each need a single exchange with lane ^ 32 (device_common.h).
@@ -109,30 +112,29 @@ __global__ __launch_bounds__(256, 1) void qkv_quant_kernel(const QkvParams p) {
   const int wk = tid & 7;
   const int wcb = tid >> 3;
 
-  const uint16_t* xbase[8];
-  bool xvalid[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t t = tok0 + xr + 32 * i;
-    xvalid[i] = t < p.n_tokens;
-    xbase[i] = p.x + (xvalid[i] ? t : 0) * p.ldx + 8 * xc;
-  }
-  const uint16_t* wbase = p.w + (int64_t)(8 * wk) * p.ldw + col0 + 8 * wcb;
+  // x rows past the end of the sequence read as zero through the buffer's size
+  const int64_t rows_valid = min((int64_t)kBN, p.n_tokens - tok0);
+  const __amdgpu_buffer_rsrc_t xr_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.x + tok0 * p.ldx), 0, (int32_t)(rows_valid * p.ldx * 2), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t wr_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.w + col0), 0, (int32_t)0x7fffffff, kBufferWord3);
+  const uint32_t x_off = (uint32_t)((xr * p.ldx + 8 * xc) * 2);
+  const uint32_t x_rowstep = (uint32_t)(32 * p.ldx * 2);
+  const uint32_t w_off = (uint32_t)(((8 * wk) * p.ldw + 8 * wcb) * 2);
+  const uint32_t w_rowstep = (uint32_t)(p.ldw * 2);
 
-  u32x4 xreg[8], wreg[8];
-  auto load_tiles = [&](int kt) {
-    const int64_t k0 = (int64_t)kt * kBK;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (xvalid[i]) v = *reinterpret_cast<const u32x4*>(xbase[i] + k0);
-      xreg[i] = v;
-    }
+  u32x4 xregs[2][8], wregs[2][8];
+  auto load_tiles = [&](int kt, u32x4 (&xreg)[8], u32x4 (&wreg)[8]) {
+    const int32_t kx = kt * kBK * 2;                       // byte offset along k in x rows
+    const int32_t kw = (int32_t)((int64_t)kt * kBK * p.ldw * 2);  // byte offset of k rows in W
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      wreg[i] = *reinterpret_cast<const u32x4*>(wbase + (k0 + i) * p.ldw);
+      xreg[i] = __builtin_amdgcn_raw_buffer_load_b128(xr_rsrc, x_off + i * x_rowstep, kx, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      wreg[i] = __builtin_amdgcn_raw_buffer_load_b128(wr_rsrc, w_off + i * w_rowstep, kw, 0);
   };
-  auto store_tiles = [&](int stage) {
+  auto store_tiles = [&](int stage, const u32x4 (&xreg)[8], const u32x4 (&wreg)[8]) {
     uint16_t* sA = lds[stage][0];
     uint16_t* sB = lds[stage][1];
 #pragma unroll
@@ -161,34 +163,62 @@ __global__ __launch_bounds__(256, 1) void qkv_quant_kernel(const QkvParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
 
-  const int nk = p.d_model / kBK;
-  load_tiles(0);
-  store_tiles(0);
+  const int nk = p.d_model / kBK;   // a multiple of 4 (d is a multiple of 256)
+  load_tiles(0, xregs[0], wregs[0]);
+  load_tiles(1, xregs[1], wregs[1]);
+  store_tiles(0, xregs[0], wregs[0]);
+  load_tiles(2, xregs[0], wregs[0]);
   __syncthreads();
   const int a_row = (128 * wc + l32) * kStride + 8 * hsel;
   const int b_row = (128 * wt + l32) * kStride + 8 * hsel;
-  for (int kt = 0; kt < nk; ++kt) {
+  // slices are loaded two iterations before they are written to LDS: at the end of
+  // iteration kt the registers holding slice kt + 1 are stored, then reloaded with
+  // slice kt + 3 (clamped to the last slice near the end)
+  auto iteration = [&](int kt, u32x4 (&xreg)[8], u32x4 (&wreg)[8]) {
     const int stage = kt & 1;
-    if (kt + 1 < nk) load_tiles(kt + 1);
     const uint16_t* sA = lds[stage][0];
     const uint16_t* sB = lds[stage][1];
+    bf16x8 af[2][4], bfr[2][4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      af[0][c] = *reinterpret_cast<const bf16x8*>(sA + a_row + 32 * c * kStride);
+      bfr[0][c] = *reinterpret_cast<const bf16x8*>(sB + b_row + 32 * c * kStride);
+    }
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8 af[4], bfr[4];
+      const int cur = ks & 1;
+      if (ks + 1 < kBK / 16) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        af[c] = *reinterpret_cast<const bf16x8*>(sA + a_row + 32 * c * kStride + 16 * ks);
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        bfr[t] = *reinterpret_cast<const bf16x8*>(sB + b_row + 32 * t * kStride + 16 * ks);
+        for (int c = 0; c < 4; ++c) {
+          af[cur ^ 1][c] = *reinterpret_cast<const bf16x8*>(sA + a_row + 32 * c * kStride + 16 * (ks + 1));
+          bfr[cur ^ 1][c] = *reinterpret_cast<const bf16x8*>(sB + b_row + 32 * c * kStride + 16 * (ks + 1));
+        }
+      }
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          acc[c][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c], bfr[t], acc[c][t], 0, 0, 0);
+          acc[c][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][c], bfr[cur][t], acc[c][t], 0, 0, 0);
     }
-    if (kt + 1 < nk) store_tiles(stage ^ 1);
+    store_tiles(stage ^ 1, xreg, wreg);
+    load_tiles(min(kt + 3, nk - 1), xreg, wreg);
+    // schedule: first-step fragments; then per step its 16 MFMAs with the next step's
+    // 8 fragment reads threaded between them; LDS writes and global loads last
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (ks + 1 < kBK / 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
     __syncthreads();
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    iteration(kt, xregs[1], wregs[1]);
+    iteration(kt + 1, xregs[0], wregs[0]);
   }
 
   // ---- epilogue: one head x 128 tokens per wave

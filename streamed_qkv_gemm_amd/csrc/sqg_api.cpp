@@ -204,6 +204,8 @@ SQG_API int sqg_streamed_qkv_quant(const sqg_qkv_args* a, void* stream) {
   const int64_t d = a->d_model;
   if (d % 256 != 0)
     return fail(SQG_ERR_UNSUPPORTED, "d_model must be a multiple of 256 (got %lld)", (long long)d);
+  if (d * a->ldw * 2 > 0x7fffffffLL || 256 * a->ldx * 2 > 0x7fffffffLL)
+    return fail(SQG_ERR_UNSUPPORTED, "W (or a 256-row slice of x) exceeds the 2 GiB a buffer resource addresses");
   if (a->reserved != 0) return fail(SQG_ERR_INVALID_ARGUMENT, "reserved field not 0");
   if ((a->q_norm_w == nullptr) != (a->k_norm_w == nullptr))
     return fail(SQG_ERR_INVALID_ARGUMENT, "q_norm_w and k_norm_w must both be set or both be NULL");
