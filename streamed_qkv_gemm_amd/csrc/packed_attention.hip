@@ -26,7 +26,10 @@
 //   O^T += V_r^T P^T       (dims x queries)
 // The transposed products keep a query's scores and its 128 output values in one
 // lane pair, so the softmax statistics and the final inverse rotation are
-// register-local apart from one exchange with lane ^ 32.  The running maximum is
+// register-local apart from one exchange with lane ^ 32 (v_permlane32_swap inside
+// the loop).  The query's high part stays in registers; its remainder waits in LDS
+// next to the tiles, and both K and V fragments are read one MFMA step ahead into
+// a second register set, so the LDS latency hides behind the running MFMAs.  The running maximum is
 // only moved (and O rescaled) when a column's maximum grows by more than 2^8, so
 // most tiles skip the rescale; P then stays below 256, well inside f16.
 #include "device_common.h"
@@ -99,10 +102,11 @@ struct TileRegs {
 __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(16))) _Float16 sK[2][kKTile];
   __shared__ __attribute__((aligned(16))) _Float16 sV[2][kVTile];
+  __shared__ __attribute__((aligned(16))) _Float16 sQl[kWaves][32 * kHeadDim];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31;
   const int hsel = lane >> 5;
   const int head = blockIdx.y;
@@ -159,7 +163,11 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
         qf[ks][j] = hi;
         ql[ks][j] = (_Float16)(r - (float)hi);
       }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      *reinterpret_cast<f16x8*>(&sQl[wave][(ks * 64 + lane) * 8]) = ql[ks];
   }
+  const _Float16* qlw = sQl[wave];
 
   // ---- per-thread maps for the K/V tile loads (64 keys per tile, 512 threads)
   const int kkey = tid >> 3;   // K: key of the tile, dims 16 kpart .. + 15
@@ -175,53 +183,60 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
   const uint32_t v_off8 = (uint32_t)(4 * vq * 128 + 4 * vd);
   const uint32_t vs_off = (uint32_t)(2 * (4 * vq * 4 + (vd >> 3)));
 
-  // Tile loads go through buffer resources whose base is the tile's first key
-  // (wave-uniform, scalar registers) and whose size ends at the head's last row of
-  // the segment: each thread adds a constant offset, and rows past the end of the
-  // segment (the ragged tail of the sequence) read as zero.
+  // Tile loads go through buffer resources that cover this head's rows of one
+  // segment (codes) or of the whole sequence (scales); rows past the end read as
+  // zero.  The load cursor below follows the segment of the next tile to load in
+  // scalar registers, so a tile costs a few scalar adds and one vector add per base.
+  const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.kscale + (int64_t)head * N * 4), 0, (int32_t)(N * 8), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vsr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.vscale + (int64_t)head * N * 4), 0, (int32_t)(N * 8), kBufferWord3);
+  int ld_seg = -1;
+  int64_t ld_sb = 0, ld_se = 0;
+  int ld_fmt = FMT_INT4;
+  __amdgpu_buffer_rsrc_t kr = ksr, vr = vsr;
   auto load_tile = [&](int64_t key0, TileRegs& r) {
-    const int seg = find_segment(p.seg, key0);
-    const int fmt = p.seg.fmt[seg];
-    const int64_t sb = p.seg.begin[seg];
-    const int64_t se = p.seg.end[seg];
-    const int rb = fmt == FMT_INT4 ? 64 : 128;
-    const int64_t row0 = (int64_t)head * (se - sb) + (key0 - sb);   // first key's row
-    const int32_t code_bytes = (int32_t)((se - key0) * rb);
-    const int32_t scale_bytes = (int32_t)((N - key0) * 8);
-    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.kpack + p.seg.offset[seg] + row0 * rb), 0, code_bytes, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.vpack + p.seg.offset[seg] + row0 * rb), 0, code_bytes, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.kscale + ((int64_t)head * N + key0) * 4), 0, scale_bytes, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t vsr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.vscale + ((int64_t)head * N + key0) * 4), 0, scale_bytes, kBufferWord3);
-    r.fmt = fmt;
-    r.kscale = __builtin_amdgcn_raw_buffer_load_b16(ksr, ks_off, 0, 0);
+    while (key0 >= ld_se) {  // the tile starts a new segment (rare)
+      ++ld_seg;
+      ld_sb = p.seg.begin[ld_seg];
+      ld_se = p.seg.end[ld_seg];
+      ld_fmt = p.seg.fmt[ld_seg];
+      const int64_t rb = ld_fmt == FMT_INT4 ? 64 : 128;
+      const int64_t base = p.seg.offset[ld_seg] + (int64_t)head * (ld_se - ld_sb) * rb;
+      const int32_t bytes = (int32_t)((ld_se - ld_sb) * rb);
+      kr = __builtin_amdgcn_make_buffer_rsrc((void*)(p.kpack + base), 0, bytes, kBufferWord3);
+      vr = __builtin_amdgcn_make_buffer_rsrc((void*)(p.vpack + base), 0, bytes, kBufferWord3);
+    }
+    const uint32_t srow = (uint32_t)(key0 * 8);
+    r.fmt = ld_fmt;
+    r.kscale = __builtin_amdgcn_raw_buffer_load_b16(ksr, ks_off + srow, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r.vscale[j] = __builtin_amdgcn_raw_buffer_load_b16(vsr, vs_off + 8 * j, 0, 0);
-    if (fmt == FMT_INT4) {
-      const u32x2 cw = __builtin_amdgcn_raw_buffer_load_b64(kr, k_off4, 0, 0);
+    for (int j = 0; j < 4; ++j) r.vscale[j] = __builtin_amdgcn_raw_buffer_load_b16(vsr, vs_off + srow + 8 * j, 0, 0);
+    if (ld_fmt == FMT_INT4) {
+      const uint32_t crow = (uint32_t)((key0 - ld_sb) * 64);
+      const u32x2 cw = __builtin_amdgcn_raw_buffer_load_b64(kr, k_off4 + crow, 0, 0);
       r.k[0] = cw[0];
       r.k[1] = cw[1];
       r.k[2] = 0u;
       r.k[3] = 0u;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) r.v[j] = __builtin_amdgcn_raw_buffer_load_b16(vr, v_off4 + 64 * j, 0, 0);
+      for (int j = 0; j < 4; ++j) r.v[j] = __builtin_amdgcn_raw_buffer_load_b16(vr, v_off4 + crow + 64 * j, 0, 0);
     } else {
-      r.k = __builtin_amdgcn_raw_buffer_load_b128(kr, k_off8, 0, 0);
+      const uint32_t crow = (uint32_t)((key0 - ld_sb) * 128);
+      r.k = __builtin_amdgcn_raw_buffer_load_b128(kr, k_off8 + crow, 0, 0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) r.v[j] = __builtin_amdgcn_raw_buffer_load_b32(vr, v_off8 + 128 * j, 0, 0);
+      for (int j = 0; j < 4; ++j) r.v[j] = __builtin_amdgcn_raw_buffer_load_b32(vr, v_off8 + crow + 128 * j, 0, 0);
     }
   };
 
   auto store_tile = [&](const TileRegs& r, int stage) {
     _Float16* K = sK[stage];
     _Float16* V = sV[stage];
+    const int fmt = __builtin_amdgcn_readfirstlane(r.fmt);
     const uint32_t ks2 = r.kscale | (r.kscale << 16);
     // K: 16 values of (key, part) -> row kkey, elements 16 kpart ..
     uint32_t o[8];
-    if (r.fmt == FMT_INT4) {
+    if (fmt == FMT_INT4) {
       uint32_t a[4], b[4];
       dequant_int4x8(r.k[0], ks2, a);
       dequant_int4x8(r.k[1], ks2, b);
@@ -249,7 +264,7 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
     for (int j = 0; j < 4; ++j) {
       const uint32_t s2 = r.vscale[j] | (r.vscale[j] << 16);
       uint32_t cw[4];
-      if (r.fmt == FMT_INT4) {
+      if (fmt == FMT_INT4) {
         dequant_int4x8(r.v[j], s2, cw);   // codes 0..3 sit in the low 16 bits
       } else {
         uint32_t c8[2];
@@ -301,20 +316,27 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
   const bool lead = wave < kWaves / 2;
 
   auto do_qk = [&](int stage, f32x16 (&s)[kKB]) {
-#pragma unroll
-    for (int a = 0; a < kKB; ++a)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[a][e] = 0.0f;
     const _Float16* K = sK[stage];
+    // fragments of k-step ks+1 are read while the four MFMAs of step ks run
+    f16x8 kf[2][kKB], lo[2];
+    auto rd = [&](int ks, int b) {
+      lo[b] = *reinterpret_cast<const f16x8*>(qlw + (ks * 64 + lane) * 8);
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb)
+        kf[b][kb] = *reinterpret_cast<const f16x8*>(K + (32 * kb + l32) * kKStride + 16 * ks + 8 * hsel);
+    };
+    rd(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
+      if (ks < 7) rd(ks + 1, (ks + 1) & 1);
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb) {
-        const f16x8 kf =
-            *reinterpret_cast<const f16x8*>(K + (32 * kb + l32) * kKStride + 16 * ks + 8 * hsel);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], s[kb], 0, 0, 0);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, ql[ks], s[kb], 0, 0, 0);
+        const f32x16 acc = ks == 0 ? f32x16{} : s[kb];
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks & 1][kb], qf[ks], acc, 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks & 1][kb], lo[ks & 1], s[kb], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -333,7 +355,10 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
     for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-    mx = fmaxf(mx, xor32(mx)) * c;
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+    }
     if (__any(mx > m_run + kRescaleLog2)) {  // wave-uniform: move every column's max
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -359,14 +384,21 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
 
   auto do_pv = [&](int stage, const f16x8 (&pf)[2 * kKB]) {
     const _Float16* V = sV[stage];
+    f16x8 vf[2][4];
+    auto rd = [&](int ks, int b) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        vf[b][db] = *reinterpret_cast<const f16x8*>(V + (32 * db + l32) * kVStride + 16 * ks + 8 * hsel);
+    };
+    rd(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < 2 * kKB; ++ks) {
+      if (ks + 1 < 2 * kKB) rd(ks + 1, (ks + 1) & 1);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const f16x8 vf =
-            *reinterpret_cast<const f16x8*>(V + (32 * db + l32) * kVStride + 16 * ks + 8 * hsel);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[ks], oacc[db], 0, 0, 0);
-      }
+      for (int db = 0; db < 4; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[ks & 1][db], pf[ks], oacc[db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
