@@ -23,6 +23,15 @@ METRIC = "packed-KV attention TFLOP/s + streamed QKV-quant tokens/s; peak HBM by
 PEAK_TFLOPS_F16 = 2500.0   # MI355X dense bf16 / f16 MFMA (published)
 DEFAULT_WORKLOAD = "h3_217k_normrope"
 
+# HBM bytes per launch of the attention kernel, from rocprofv3 FETCH_SIZE and WRITE_SIZE
+# counters scaled by the same counters on a device copy of known size, keyed by the
+# SHA-256 of the kernel source they were taken on and by the workload.  A changed
+# kernel reports null until the counters are taken again.
+MEASURED_TRAFFIC = {
+    # profiles/hbm_traffic_packed_attention_h3_217k_normrope.md
+    ("aaa5968a00a4c6c5c79467ec6dbcf6a50d9ab3c569c1e481e1281ac3d83cd5cd", "h3_217k_normrope"): 1.9922e10,
+}
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -33,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=4, help="heads in the oracle's attention sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed steps, copy this many MiB device-to-device three times "
+                         "(reference dispatches for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -101,6 +113,15 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     peak_alloc = torch.cuda.max_memory_allocated(dev)
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 2
+        src = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] copy calibration: 3 x %d bytes read + written" % (2 * n), file=sys.stderr)
+        del src, dst
     qkv_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     att_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     step_ms = sum(e[0].elapsed_time(e[2]) for e in evs) / args.steps
@@ -174,7 +195,7 @@ def main():
             "peak": PEAK_TFLOPS_F16,
             "unit": "TFLOP/s",
             "frac": att_tflops / PEAK_TFLOPS_F16,
-            "traffic": None,
+            "traffic": attention_traffic(wl.name),
             "launches_per_step": n_att_launch,
             "avg_launch_ms": att_ms / n_att_launch,
             "algorithmic_flop_per_step": att_flop,
@@ -189,6 +210,15 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, x, w, norm, store, args.cpu_heads)
     print(json.dumps(result), flush=True)
+
+
+def attention_traffic(workload):
+    """HBM bytes per attention launch measured on this exact kernel source, else None."""
+    import hashlib
+    path = os.path.join(ROOT, "streamed_qkv_gemm_amd", "csrc", "packed_attention.hip")
+    with open(path, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    return MEASURED_TRAFFIC.get((sha, workload))
 
 
 def cpu_baseline(wl, x, w, norm, store, n_heads_sample):
