@@ -31,7 +31,7 @@ constexpr int kBN = 256;        // tokens per workgroup
 constexpr int kBK = 64;         // reduction slice per stage
 constexpr int kStride = kBK + 8;  // bf16 per LDS row (144 B: conflict-free 16-byte reads)
 constexpr int kTileElems = 256 * kStride;
-constexpr int kGroupRows = 16;  // token tiles per raster group (L2 reuse of W and x)
+constexpr int kGroupRows = 32;  // token tiles per raster group (L2 reuse of W and x)
 
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
   return __builtin_amdgcn_perm(hi_src, lo_src, sel);
