@@ -331,3 +331,23 @@ def test_attention_deterministic(lib):
     b, lb = lib.packed_kv_attention(store)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_zero_query_gives_mean_of_values(lib):
+    # Q = 0: every score is 0, the weights are uniform, O = mean of the decoded values
+    # (model basis) and LSE = ln(N) exactly; checked against that closed form, not the
+    # oracle's attention.  N = 1000 spans 16 key tiles with a ragged tail and an INT8 range.
+    N, d = 1000, 512
+    ranges = [(0, 256, INT8), (256, N, INT4)]
+    store, layout, H = attention_case(lib, N, d, ranges, seed=131)
+    store["q"] = torch.zeros_like(store["q"])
+    o, lse = lib.packed_kv_attention(store)
+    torch.cuda.synchronize()
+    R = oracle.rotation_matrix()
+    vp, vs = host(store["vpack"]), host(store["vscale"])
+    for h in range(H):
+        v = oracle.decode_head(vp, vs, layout, H, h, 0, N) @ R.T
+        want = v.mean(axis=0)
+        got = host(o)[:, h * 128:(h + 1) * 128].astype(np.float64)
+        assert np.abs(got - want[None, :]).max() <= 1e-3 * max(1.0, np.abs(want).max())
+    assert np.allclose(host(lse), math.log(N), rtol=0, atol=1e-4)
