@@ -29,7 +29,7 @@ DEFAULT_WORKLOAD = "h3_217k_normrope"
 # kernel reports null until the counters are taken again.
 MEASURED_TRAFFIC = {
     # profiles/hbm_traffic_packed_attention_h3_217k_normrope.md
-    ("aaa5968a00a4c6c5c79467ec6dbcf6a50d9ab3c569c1e481e1281ac3d83cd5cd", "h3_217k_normrope"): 1.9922e10,
+    ("ec9e9ca77ec6b86694383f3e383f549627be92f4eb65fcd7d6f74e3dcd38deb9", "h3_217k_normrope"): 1.9885e10,
 }
 
 
@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=4, help="heads in the oracle's attention sample")
+    ap.add_argument("--qrecompute-steps", type=int, default=1,
+                    help="steps of the Q-recompute variant timed after the main steps (0 = skip)")
+    ap.add_argument("--q-chunk-rows", type=int, default=0, help="query chunk of the Q-recompute variant")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, copy this many MiB device-to-device three times "
                          "(reference dispatches for HBM byte counters)")
@@ -135,6 +138,46 @@ def main():
     att_tflops = att_flop / (att_ms * 1e-3) / 1e12
     qkv_tflops = qkv_flop / (qkv_ms * 1e-3) / 1e12
 
+    # ---- Q-recompute variant: K/V-only projection, then Q rebuilt per query chunk inside
+    # the attention call; no [N, d] Q buffer exists (timed separately, not part of value)
+    qrec = None
+    if args.qrecompute_steps > 0:
+        kv_store = sqg.alloc_store(N, d, wl.ranges, device=dev, emit=sqg.SQG_EMIT_KV)
+        ws_bytes = sqg.qrecompute_workspace_bytes(N, d, args.q_chunk_rows)
+        ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+        q_kw = {k: v for k, v in kw.items() if k != "k_norm_w"}
+
+        def qrec_step(ev=None):
+            if ev:
+                ev[0].record(stream)
+            sqg.streamed_qkv_quant(x, w, ranges=wl.ranges, chunk_rows=wl.chunk_rows, out=kv_store,
+                                   emit=sqg.SQG_EMIT_KV, **kw)
+            if ev:
+                ev[1].record(stream)
+            sqg.packed_kv_attention_qrecompute(kv_store, x, w, q_chunk_rows=args.q_chunk_rows,
+                                               workspace=ws, kv_block=wl.kv_block, o=o, lse=lse, **q_kw)
+            if ev:
+                ev[2].record(stream)
+
+        qrec_step()
+        torch.cuda.synchronize()
+        qev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+               for _ in range(args.qrecompute_steps)]
+        for i in range(args.qrecompute_steps):
+            qrec_step(qev[i])
+        torch.cuda.synchronize()
+        kv_ms = sum(e[0].elapsed_time(e[1]) for e in qev) / args.qrecompute_steps
+        qa_ms = sum(e[1].elapsed_time(e[2]) for e in qev) / args.qrecompute_steps
+        qrec_ws = 2 * L["pack_bytes"] + 2 * L["scale_bytes"] + ws_bytes
+        qrec = {"steps": args.qrecompute_steps, "ms_per_step": kv_ms + qa_ms,
+                "tflops": (qkv_flop + att_flop) / ((kv_ms + qa_ms) * 1e-3) / 1e12,
+                "kv_quant_ms": kv_ms, "q_recompute_attention_ms": qa_ms,
+                "q_chunk_rows": ws_bytes // (2 * d), "workspace_bytes": ws_bytes,
+                "qkv_working_set_bytes": qrec_ws,
+                "working_set_ratio": qrec_ws / L["bf16_qkv_bytes"]}
+        del kv_store, ws
+        torch.cuda.empty_cache()
+
     # ---- bf16-materialising baseline: x @ W into a bf16 [N, 3d] tensor (library GEMM)
     bf16_base = None
     if not args.no_bf16_baseline:
@@ -187,6 +230,7 @@ def main():
         "bf16_qkv_bytes": L["bf16_qkv_bytes"],
         "working_set_ratio": packed_ws / L["bf16_qkv_bytes"],
         "bf16_materialising_baseline": bf16_base,
+        "qrecompute": qrec,
         "wall_s_timed": wall,
         "roofline": {
             "kernel": "packed_attention_kernel",

@@ -60,6 +60,16 @@ typedef enum sqg_kv_format {
 
 typedef enum sqg_out_dtype { SQG_F32 = 0, SQG_BF16 = 1, SQG_F16 = 2 } sqg_out_dtype;
 
+/* What one sqg_streamed_qkv_quant call writes.  [VL] block section (the three-phase
+ * streamed block): phase 1 keeps only K and V for the whole sequence and phase 2
+ * recomputes Q chunk by chunk; SQG_EMIT_KV is that phase 1, SQG_EMIT_Q the Q part of
+ * phase 2 (see sqg_packed_kv_attention_qrecompute). */
+typedef enum sqg_emit {
+  SQG_EMIT_QKV = 0,   /* Q and the packed K/V store */
+  SQG_EMIT_Q = 1,     /* Q only: kpack, vpack, kscale, vscale may be NULL */
+  SQG_EMIT_KV = 2     /* the packed K/V store only: q may be NULL */
+} sqg_emit;
+
 /* One token range [begin, end) of the precision policy. */
 typedef struct sqg_range {
   int64_t begin;
@@ -105,7 +115,7 @@ typedef struct sqg_qkv_args {
   const float* rope_sin;
   const sqg_range* ranges;     /* host; NULL with n_ranges 0 = all INT4 */
   int32_t n_ranges;
-  int32_t reserved;
+  int32_t emit;                /* sqg_emit (0 = Q and K/V) */
   int64_t chunk_rows;          /* rows per launch (multiple of 128); 0 = one launch */
   int64_t min_tail;            /* a last chunk shorter than this joins the previous one; <0 = 512 */
   void* q;                     /* device, bf16 [N, ldq] out (model basis) */
@@ -142,6 +152,27 @@ typedef struct sqg_attn_args {
                                   required when accumulate or kv_block > 0 */
 } sqg_attn_args;
 
+/* Arguments of sqg_packed_kv_attention_qrecompute. */
+typedef struct sqg_qrecompute_args {
+  sqg_attn_args attn;          /* as for sqg_packed_kv_attention, except that attn.q and attn.ldq
+                                  are ignored: Q is recomputed into the workspace */
+  const void* x;               /* device, bf16 [N, ldx]: the rows the K/V store was built from */
+  int64_t ldx;
+  const void* w_qkv;           /* device, bf16 [d, 3d] row-major (only the q columns are read) */
+  int64_t ldw;
+  const float* q_norm_w;       /* device, fp32 [128] or NULL: per-head RMSNorm gain of q */
+  const float* rope_cos;       /* device, fp32 [N, 64] or NULL (both or neither) */
+  const float* rope_sin;
+  float eps;                   /* RMSNorm epsilon */
+  int32_t reserved;            /* must be 0 */
+  int64_t q_chunk_rows;        /* query rows per chunk, a multiple of 128; 0 = the larger of
+                                  16384 and 256 * ceil(2048 / n_heads); a last chunk shorter
+                                  than 512 joins the previous one */
+  void* workspace;             /* device, bf16 Q of one chunk; at least
+                                  sqg_qrecompute_workspace_bytes(...) bytes */
+  int64_t workspace_bytes;
+} sqg_qrecompute_args;
+
 /* Library version (SQG_VERSION of the build). */
 SQG_API int sqg_version(void);
 
@@ -152,7 +183,8 @@ SQG_API const char* sqg_status_string(int status);
 SQG_API const char* sqg_last_error(void);
 
 /* sizeof of the argument structs, so bindings can check their mirrors:
- * which = 0 sqg_range, 1 sqg_layout, 2 sqg_qkv_args, 3 sqg_attn_args; else -1. */
+ * which = 0 sqg_range, 1 sqg_layout, 2 sqg_qkv_args, 3 sqg_attn_args,
+ * 4 sqg_qrecompute_args; else -1. */
 SQG_API int64_t sqg_struct_size(int which);
 
 /* Host only.  Row chunks of `size` rows over [0, n); a last chunk shorter than
@@ -186,7 +218,9 @@ SQG_API int sqg_rope_table(int64_t pos0, int64_t n, double theta, float* cos_out
  *   - K and V: r = u H / sqrt(128) (Sylvester Hadamard, [VL] kvi8r `_hadamard`),
  *     per group of 32: s = fp16(max|r| / qmax), code = clamp(rne(r / s), +-qmax)
  *     (qmax 7 for INT4, 127 for INT8 ranges), packed per sqg_kv_layout.
- * Chunks only partition the launches: results do not depend on chunk_rows. */
+ * Chunks only partition the launches: results do not depend on chunk_rows.  `emit`
+ * restricts the launch to Q or to the K/V store; what it writes is identical to the
+ * same part of a full call. */
 SQG_API int sqg_streamed_qkv_quant(const sqg_qkv_args* args, void* stream);
 
 /* Flash-style attention that reads the packed K/V tile by tile ([FR] "Proposed
@@ -200,6 +234,23 @@ SQG_API int sqg_streamed_qkv_quant(const sqg_qkv_args* args, void* stream);
  * accumulate = 1 merges into the (O, lse) already in the buffers (requires
  * o_dtype SQG_F32). */
 SQG_API int sqg_packed_kv_attention(const sqg_attn_args* args, void* stream);
+
+/* Host only.  Bytes of the Q workspace sqg_packed_kv_attention_qrecompute needs for
+ * query rows [q_begin, q_end) (n_query_rows = q_end - q_begin) in chunks of
+ * q_chunk_rows (0 = the default of sqg_qrecompute_args) at d_model: the largest chunk's
+ * rows * d_model * 2.  Returns -1 for invalid arguments. */
+SQG_API int64_t sqg_qrecompute_workspace_bytes(int64_t n_query_rows, int64_t q_chunk_rows,
+                                               int32_t d_model);
+
+/* Attention with Q recomputed per query chunk ([VL] block sections `_phase2_q_attn`
+ * and the three-phase streamed block): for each chunk of q_chunk_rows query rows,
+ * Q = bf16 of the projection of those rows (with the same RMSNorm / RoPE as
+ * sqg_streamed_qkv_quant) is written to the workspace and the chunk attends to the
+ * packed store exactly as sqg_packed_kv_attention does.  With a store written by
+ * SQG_EMIT_KV, no [N, d] Q buffer exists: the device working set is the K/V store
+ * plus one chunk of Q.  Results equal sqg_streamed_qkv_quant (SQG_EMIT_Q) followed by
+ * sqg_packed_kv_attention bit for bit. */
+SQG_API int sqg_packed_kv_attention_qrecompute(const sqg_qrecompute_args* args, void* stream);
 
 /* Test entry: runs the kernels' own quantise-and-pack step on fp32 rotated vectors
  * r (device, [rows, 128]) with format fmt for every row; writes codes (device,

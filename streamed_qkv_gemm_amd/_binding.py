@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(PKG, "libsqg.so")
 SQG_INT4_ROT = 0
 SQG_INT8_ROT = 1
 SQG_F32, SQG_BF16, SQG_F16 = 0, 1, 2
+SQG_EMIT_QKV, SQG_EMIT_Q, SQG_EMIT_KV = 0, 1, 2
 MAX_SEGMENTS = 16
 HEAD_DIM = 128
 
@@ -50,7 +51,7 @@ class QkvArgs(ctypes.Structure):
                 ("x", _vp), ("ldx", _c_i64), ("w_qkv", _vp), ("ldw", _c_i64),
                 ("q_norm_w", _vp), ("k_norm_w", _vp), ("eps", ctypes.c_float),
                 ("rope_cos", _vp), ("rope_sin", _vp),
-                ("ranges", ctypes.POINTER(Range)), ("n_ranges", _c_i32), ("reserved", _c_i32),
+                ("ranges", ctypes.POINTER(Range)), ("n_ranges", _c_i32), ("emit", _c_i32),
                 ("chunk_rows", _c_i64), ("min_tail", _c_i64),
                 ("q", _vp), ("ldq", _c_i64), ("kpack", _vp), ("vpack", _vp),
                 ("kscale", _vp), ("vscale", _vp)]
@@ -64,6 +65,13 @@ class AttnArgs(ctypes.Structure):
                 ("q_begin", _c_i64), ("q_end", _c_i64), ("kv_begin", _c_i64), ("kv_end", _c_i64),
                 ("kv_block", _c_i64), ("accumulate", _c_i32), ("softmax_scale", ctypes.c_float),
                 ("o", _vp), ("ldo", _c_i64), ("lse", _vp)]
+
+
+class QRecomputeArgs(ctypes.Structure):
+    _fields_ = [("attn", AttnArgs), ("x", _vp), ("ldx", _c_i64), ("w_qkv", _vp), ("ldw", _c_i64),
+                ("q_norm_w", _vp), ("rope_cos", _vp), ("rope_sin", _vp), ("eps", ctypes.c_float),
+                ("reserved", _c_i32), ("q_chunk_rows", _c_i64), ("workspace", _vp),
+                ("workspace_bytes", _c_i64)]
 
 
 _lib = None
@@ -92,9 +100,12 @@ def load(path: Optional[str] = None):
     lib.sqg_rope_table.argtypes = [_c_i64, _c_i64, ctypes.c_double, _vp, _vp]
     lib.sqg_streamed_qkv_quant.argtypes = [ctypes.POINTER(QkvArgs), _vp]
     lib.sqg_packed_kv_attention.argtypes = [ctypes.POINTER(AttnArgs), _vp]
+    lib.sqg_qrecompute_workspace_bytes.restype = _c_i64
+    lib.sqg_qrecompute_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i32]
+    lib.sqg_packed_kv_attention_qrecompute.argtypes = [ctypes.POINTER(QRecomputeArgs), _vp]
     lib.sqg_test_quant_pack_f32.argtypes = [_vp, _c_i64, _c_i32, _vp, _vp, _vp]
     lib.sqg_test_fwht_f32.argtypes = [_vp, _vp, _c_i64, _c_i32, _vp]
-    for name, cls in ((0, Range), (1, Layout), (2, QkvArgs), (3, AttnArgs)):
+    for name, cls in ((0, Range), (1, Layout), (2, QkvArgs), (3, AttnArgs), (4, QRecomputeArgs)):
         got = lib.sqg_struct_size(name)
         if got != ctypes.sizeof(cls):
             raise RuntimeError("ABI mismatch: %s is %d bytes in the library, %d in the binding"
@@ -170,18 +181,25 @@ def rope_table(n_tokens: int, theta: float = 10000.0, pos0: int = 0, device="cud
     return cos.to(device), sin.to(device)
 
 
-def alloc_store(n_tokens: int, d_model: int, ranges=None, device="cuda"):
-    """Empty output buffers of the streamed QKV-quant: Q, packed K/V and scales."""
+def alloc_store(n_tokens: int, d_model: int, ranges=None, device="cuda", emit: int = SQG_EMIT_QKV):
+    """Empty output buffers of the streamed QKV-quant: Q, packed K/V and scales.
+
+    With emit SQG_EMIT_KV there is no Q buffer ("q" is None); with SQG_EMIT_Q no
+    packed store."""
     L = kv_layout(n_tokens, d_model, ranges)
     H = d_model // HEAD_DIM
+    want_q, want_kv = emit != SQG_EMIT_KV, emit != SQG_EMIT_Q
+    empty = lambda *shape, dtype: torch.empty(shape, dtype=dtype, device=device)  # noqa: E731
     return {
-        "q": torch.empty((n_tokens, d_model), dtype=torch.bfloat16, device=device),
-        "kpack": torch.empty((max(L["pack_bytes"], 16),), dtype=torch.uint8, device=device),
-        "vpack": torch.empty((max(L["pack_bytes"], 16),), dtype=torch.uint8, device=device),
-        "kscale": torch.empty((H, n_tokens, 4), dtype=torch.float16, device=device),
-        "vscale": torch.empty((H, n_tokens, 4), dtype=torch.float16, device=device),
+        "q": empty(n_tokens, d_model, dtype=torch.bfloat16) if want_q else None,
+        "kpack": empty(max(L["pack_bytes"], 16), dtype=torch.uint8) if want_kv else None,
+        "vpack": empty(max(L["pack_bytes"], 16), dtype=torch.uint8) if want_kv else None,
+        "kscale": empty(H, n_tokens, 4, dtype=torch.float16) if want_kv else None,
+        "vscale": empty(H, n_tokens, 4, dtype=torch.float16) if want_kv else None,
         "layout": L,
         "ranges": list(ranges) if ranges else None,
+        "n_tokens": n_tokens,
+        "d_model": d_model,
     }
 
 
@@ -189,14 +207,16 @@ def streamed_qkv_quant(x: torch.Tensor, w_qkv: torch.Tensor, ranges=None, chunk_
                        min_tail: int = 512, q_norm_w: Optional[torch.Tensor] = None,
                        k_norm_w: Optional[torch.Tensor] = None, eps: float = 1e-6,
                        rope_cos: Optional[torch.Tensor] = None,
-                       rope_sin: Optional[torch.Tensor] = None, out: Optional[Dict] = None):
+                       rope_sin: Optional[torch.Tensor] = None, out: Optional[Dict] = None,
+                       emit: int = SQG_EMIT_QKV):
     """streamed_qkv_quant(x, W_qkv, range_policy) -> {q, kpack, vpack, kscale, vscale}.
 
-    x bf16 [N, d], w_qkv bf16 [d, 3d] row-major.  Enqueued on the current stream."""
+    x bf16 [N, d], w_qkv bf16 [d, 3d] row-major.  emit picks Q and K/V (default),
+    Q only or K/V only.  Enqueued on the current stream."""
     lib = load()
     N, d = x.shape
     if out is None:
-        out = alloc_store(N, d, ranges, device=x.device)
+        out = alloc_store(N, d, ranges, device=x.device, emit=emit)
     arr, nr = _ranges_array(ranges)
     a = QkvArgs()
     a.n_tokens, a.d_model, a.n_heads = N, d, d // HEAD_DIM
@@ -206,9 +226,10 @@ def streamed_qkv_quant(x: torch.Tensor, w_qkv: torch.Tensor, ranges=None, chunk_
     a.eps = eps
     a.rope_cos, a.rope_sin = _dev_ptr(rope_cos, "rope_cos"), _dev_ptr(rope_sin, "rope_sin")
     a.ranges = ctypes.cast(arr, ctypes.POINTER(Range)) if arr is not None else None
-    a.n_ranges, a.reserved = nr, 0
+    a.n_ranges, a.emit = nr, emit
     a.chunk_rows, a.min_tail = chunk_rows, min_tail
-    a.q, a.ldq = _dev_ptr(out["q"], "q"), out["q"].stride(0)
+    if out.get("q") is not None:
+        a.q, a.ldq = _dev_ptr(out["q"], "q"), out["q"].stride(0)
     a.kpack, a.vpack = _dev_ptr(out["kpack"], "kpack"), _dev_ptr(out["vpack"], "vpack")
     a.kscale, a.vscale = _dev_ptr(out["kscale"], "kscale"), _dev_ptr(out["vscale"], "vscale")
     for t, nm in ((x, "x"), (w_qkv, "w_qkv")):
@@ -219,6 +240,29 @@ def streamed_qkv_quant(x: torch.Tensor, w_qkv: torch.Tensor, ranges=None, chunk_
 
 
 _ODT = {torch.float32: SQG_F32, torch.bfloat16: SQG_BF16, torch.float16: SQG_F16}
+
+
+def _attn_args(store: Dict, N: int, d: int, device, q_begin, q_end, kv_begin, kv_end, kv_block,
+               accumulate, o, lse, o_dtype, softmax_scale, want_lse):
+    H = d // HEAD_DIM
+    if o is None:
+        o = torch.empty((N, d), dtype=o_dtype, device=device)
+    if lse is None and (want_lse or accumulate or kv_block > 0):
+        lse = torch.empty((H, N), dtype=torch.float32, device=device)
+    arr, nr = _ranges_array(store.get("ranges"))
+    a = AttnArgs()
+    a.n_tokens, a.d_model, a.n_heads = N, d, H
+    a.kpack, a.vpack = _dev_ptr(store["kpack"], "kpack"), _dev_ptr(store["vpack"], "vpack")
+    a.kscale, a.vscale = _dev_ptr(store["kscale"], "kscale"), _dev_ptr(store["vscale"], "vscale")
+    a.ranges = ctypes.cast(arr, ctypes.POINTER(Range)) if arr is not None else None
+    a.n_ranges = nr
+    a.o_dtype = _ODT[o.dtype]
+    a.q_begin, a.q_end, a.kv_begin, a.kv_end = q_begin, q_end, kv_begin, kv_end
+    a.kv_block, a.accumulate, a.softmax_scale = kv_block, int(bool(accumulate)), softmax_scale
+    a.o, a.ldo = _dev_ptr(o, "o"), o.stride(0)
+    a.lse = _dev_ptr(lse, "lse")
+    # keep the ranges array alive as long as the struct
+    return a, arr, o, lse
 
 
 def packed_kv_attention(store: Dict, q: Optional[torch.Tensor] = None, q_begin: int = 0,
@@ -232,26 +276,59 @@ def packed_kv_attention(store: Dict, q: Optional[torch.Tensor] = None, q_begin: 
     in the model basis; lse is fp32 [H, N] (natural log)."""
     lib = load()
     q = store["q"] if q is None else q
+    if q is None:
+        raise ValueError("no Q: the store was built without one, pass q=")
     N, d = q.shape
-    H = d // HEAD_DIM
-    if o is None:
-        o = torch.empty((N, d), dtype=o_dtype, device=q.device)
-    if lse is None and (want_lse or accumulate or kv_block > 0):
-        lse = torch.empty((H, N), dtype=torch.float32, device=q.device)
-    arr, nr = _ranges_array(store.get("ranges"))
-    a = AttnArgs()
-    a.n_tokens, a.d_model, a.n_heads = N, d, H
+    a, _keep, o, lse = _attn_args(store, N, d, q.device, q_begin, q_end, kv_begin, kv_end, kv_block,
+                                  accumulate, o, lse, o_dtype, softmax_scale, want_lse)
     a.q, a.ldq = _dev_ptr(q, "q"), q.stride(0)
-    a.kpack, a.vpack = _dev_ptr(store["kpack"], "kpack"), _dev_ptr(store["vpack"], "vpack")
-    a.kscale, a.vscale = _dev_ptr(store["kscale"], "kscale"), _dev_ptr(store["vscale"], "vscale")
-    a.ranges = ctypes.cast(arr, ctypes.POINTER(Range)) if arr is not None else None
-    a.n_ranges = nr
-    a.o_dtype = _ODT[o.dtype]
-    a.q_begin, a.q_end, a.kv_begin, a.kv_end = q_begin, q_end, kv_begin, kv_end
-    a.kv_block, a.accumulate, a.softmax_scale = kv_block, int(bool(accumulate)), softmax_scale
-    a.o, a.ldo = _dev_ptr(o, "o"), o.stride(0)
-    a.lse = _dev_ptr(lse, "lse")
     _check(lib.sqg_packed_kv_attention(ctypes.byref(a), _stream(q.device)))
+    return o, lse
+
+
+def qrecompute_workspace_bytes(n_query_rows: int, d_model: int, q_chunk_rows: int = 0) -> int:
+    """Bytes of Q workspace packed_kv_attention_qrecompute needs."""
+    got = load().sqg_qrecompute_workspace_bytes(n_query_rows, q_chunk_rows, d_model)
+    if got < 0:
+        raise ValueError("invalid arguments to qrecompute_workspace_bytes")
+    return got
+
+
+def packed_kv_attention_qrecompute(store: Dict, x: torch.Tensor, w_qkv: torch.Tensor,
+                                   q_norm_w: Optional[torch.Tensor] = None,
+                                   rope_cos: Optional[torch.Tensor] = None,
+                                   rope_sin: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                                   q_chunk_rows: int = 0, workspace: Optional[torch.Tensor] = None,
+                                   q_begin: int = 0, q_end: int = 0, kv_begin: int = 0,
+                                   kv_end: int = 0, kv_block: int = 0, accumulate: bool = False,
+                                   o: Optional[torch.Tensor] = None,
+                                   lse: Optional[torch.Tensor] = None, o_dtype=torch.float32,
+                                   softmax_scale: float = 0.0, want_lse: bool = True):
+    """Attention over the packed store with Q recomputed from x chunk by chunk -> (O, lse).
+
+    The store may come from streamed_qkv_quant(..., emit=SQG_EMIT_KV): no [N, d] Q
+    is ever held.  Same results as packed_kv_attention on the Q a full call writes."""
+    lib = load()
+    N, d = x.shape
+    for t, nm in ((x, "x"), (w_qkv, "w_qkv")):
+        if t.dtype != torch.bfloat16 or t.stride(-1) != 1:
+            raise ValueError("%s must be a row-major bf16 tensor" % nm)
+    a, _keep, o, lse = _attn_args(store, N, d, x.device, q_begin, q_end, kv_begin, kv_end, kv_block,
+                                  accumulate, o, lse, o_dtype, softmax_scale, want_lse)
+    n_q = (q_end if q_end else N) - q_begin
+    if workspace is None:
+        need = qrecompute_workspace_bytes(max(n_q, 0), d, q_chunk_rows)
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=x.device)
+    r = QRecomputeArgs()
+    r.attn = a
+    r.x, r.ldx = _dev_ptr(x, "x"), x.stride(0)
+    r.w_qkv, r.ldw = _dev_ptr(w_qkv, "w_qkv"), w_qkv.stride(0)
+    r.q_norm_w = _dev_ptr(q_norm_w, "q_norm_w")
+    r.rope_cos, r.rope_sin = _dev_ptr(rope_cos, "rope_cos"), _dev_ptr(rope_sin, "rope_sin")
+    r.eps, r.reserved, r.q_chunk_rows = eps, 0, q_chunk_rows
+    r.workspace = _dev_ptr(workspace, "workspace")
+    r.workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.sqg_packed_kv_attention_qrecompute(ctypes.byref(r), _stream(x.device)))
     return o, lse
 
 

@@ -34,8 +34,11 @@ struct QkvParams {
   int64_t ldx, ldw, ldq;
   int64_t n_tokens;
   int64_t row_begin, row_end;
+  int64_t q_row0;          // token t's Q goes to row t - q_row0 of q
   int32_t d_model, n_heads;
   float eps;
+  int32_t col_tile0;       // first 256-column tile of [q | k | v] this launch covers
+  int32_t n_col_tiles;     // number of column tiles it covers
   int32_t pad_;
   SegTable seg;
 };
@@ -53,6 +56,7 @@ struct AttnParams {
   int64_t ldq, ldo;
   int64_t n_tokens;
   int64_t q_begin, q_end;
+  int64_t q_row0;          // query row r is row r - q_row0 of q
   int64_t kv_begin, kv_end;
   int32_t d_model, n_heads;
   int32_t o_dtype;

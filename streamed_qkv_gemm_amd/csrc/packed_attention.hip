@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
   const bool qvalid = qrow < p.q_end;
   f16x8 qf[8], ql[8];
   {
-    const uint16_t* src = p.q + (qvalid ? qrow : 0) * p.ldq + head * kHeadDim + 8 * hsel;
+    const uint16_t* src = p.q + ((qvalid ? qrow : p.q_begin) - p.q_row0) * p.ldq + head * kHeadDim + 8 * hsel;
     // element e(ks, j) = 16 ks + 8 hsel + j: bits 0-2 = j, bit 3 = lane pair, bits 4-6 = ks
     float v[8][8];
 #pragma unroll

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256, 1) void qkv_quant_kernel(const QkvParams p) {
   const int hsel = lane >> 5;
 
   // ---- raster: groups of kGroupRows token tiles sweep all column tiles
-  const int n_col_tiles = (3 * p.d_model) / kBM;
+  const int n_col_tiles = p.n_col_tiles;
   const int64_t rows = p.row_end - p.row_begin;
   const int n_tok_tiles = (int)((rows + kBN - 1) / kBN);
   const int lin = blockIdx.x;
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256, 1) void qkv_quant_kernel(const QkvParams p) {
   const int gsize = min(kGroupRows, n_tok_tiles - first_tok);
   const int in_group = lin - group * per_group;
   const int tok_tile = first_tok + in_group % gsize;
-  const int col_tile = in_group / gsize;
+  const int col_tile = p.col_tile0 + in_group / gsize;
 
   const int col0 = col_tile * kBM;
   const int64_t tok0 = p.row_begin + (int64_t)tok_tile * kBN;
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256, 1) void qkv_quant_kernel(const QkvParams p) {
       if (p.q_norm_w) rms_norm_cols(u, p.q_norm_w, p.eps);
       if (p.rope_cos) rope_cols(u, p.rope_cos, p.rope_sin, t, valid);
       if (valid) {
-        uint16_t* qrow = p.q + t * p.ldq + h * kHeadDim + 4 * hsel;
+        uint16_t* qrow = p.q + (t - p.q_row0) * p.ldq + h * kHeadDim + 4 * hsel;
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -295,10 +295,9 @@ __global__ __launch_bounds__(256, 1) void qkv_quant_kernel(const QkvParams p) {
 }  // namespace
 
 int launch_qkv_quant(const QkvParams& p, void* stream) {
-  const int n_col_tiles = (3 * p.d_model) / kBM;
   const int64_t rows = p.row_end - p.row_begin;
   const int64_t n_tok_tiles = (rows + kBN - 1) / kBN;
-  const int64_t blocks = n_tok_tiles * n_col_tiles;
+  const int64_t blocks = n_tok_tiles * p.n_col_tiles;
   if (blocks <= 0) return 0;
   hipLaunchKernelGGL(qkv_quant_kernel, dim3((unsigned)blocks), dim3(256), 0,
                      (hipStream_t)stream, p);

@@ -128,6 +128,98 @@ int launch_status(int hip_err, const char* what) {
   return SQG_OK;
 }
 
+// Checks the attention arguments and fills the kernel parameters.  With check_q false
+// the caller supplies Q itself (a->q and a->ldq are ignored).  *empty is set when there
+// is nothing to compute.
+int attn_prepare(const sqg_attn_args* a, bool check_q, sqg::AttnParams* p, int64_t* kv_end_out,
+                 bool* empty) {
+  *empty = false;
+  sqg_layout L;
+  int st = build_layout(a->n_tokens, a->d_model, a->n_heads, a->ranges, a->n_ranges, &L);
+  if (st != SQG_OK) return st;
+  const int64_t N = a->n_tokens;
+  const int64_t d = a->d_model;
+  if (a->o_dtype != SQG_F32 && a->o_dtype != SQG_BF16 && a->o_dtype != SQG_F16)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "unknown o_dtype %d", a->o_dtype);
+  const int64_t q_end = a->q_end == 0 ? N : a->q_end;
+  const int64_t kv_end = a->kv_end == 0 ? N : a->kv_end;
+  if (a->q_begin < 0 || a->q_begin > q_end || q_end > N)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "query range [%lld, %lld) is outside [0, %lld]",
+                (long long)a->q_begin, (long long)q_end, (long long)N);
+  if (a->kv_block < 0 || a->kv_block % 128 != 0)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "kv_block must be 0 or a positive multiple of 128");
+  if (a->accumulate != 0 && a->accumulate != 1)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "accumulate must be 0 or 1");
+  if ((a->accumulate || a->kv_block > 0) && (!a->lse || a->o_dtype != SQG_F32))
+    return fail(SQG_ERR_INVALID_ARGUMENT,
+                "accumulate and kv_block > 0 need an lse buffer and o_dtype SQG_F32");
+  if (!(std::isfinite(a->softmax_scale) && a->softmax_scale >= 0.0f))
+    return fail(SQG_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+  if (N == 0 || q_end == a->q_begin) {
+    *empty = true;
+    return SQG_OK;
+  }
+  if (a->kv_begin < 0 || a->kv_begin >= kv_end || kv_end > N)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "key range [%lld, %lld) is empty or outside [0, %lld]",
+                (long long)a->kv_begin, (long long)kv_end, (long long)N);
+  if (a->kv_begin % 128 != 0)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "kv_begin must be a multiple of 128");
+  if ((check_q && !a->q) || !a->kpack || !a->vpack || !a->kscale || !a->vscale || !a->o)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "a required device pointer is NULL");
+  if ((check_q && a->ldq < d) || a->ldo < d)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "row strides must be >= d_model");
+  if ((check_q && a->ldq % 8) || a->ldo % 8)
+    return fail(SQG_ERR_MISALIGNED, "row strides must be multiples of 8");
+  const void* ptrs[] = {check_q ? a->q : nullptr, a->kpack, a->vpack, a->kscale, a->vscale, a->o, a->lse};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(SQG_ERR_MISALIGNED, "device pointer %p is not 16-byte aligned", ptr);
+
+  std::memset(p, 0, sizeof *p);
+  p->q = static_cast<const uint16_t*>(a->q);
+  p->kpack = static_cast<const uint8_t*>(a->kpack);
+  p->vpack = static_cast<const uint8_t*>(a->vpack);
+  p->kscale = static_cast<const uint16_t*>(a->kscale);
+  p->vscale = static_cast<const uint16_t*>(a->vscale);
+  p->o = a->o;
+  p->lse = a->lse;
+  p->ldq = a->ldq;
+  p->ldo = a->ldo;
+  p->n_tokens = N;
+  p->q_begin = a->q_begin;
+  p->q_end = q_end;
+  p->q_row0 = 0;
+  p->d_model = a->d_model;
+  p->n_heads = a->n_heads;
+  p->o_dtype = a->o_dtype;
+  const double scale = a->softmax_scale > 0.0f ? (double)a->softmax_scale : 1.0 / std::sqrt(128.0);
+  p->scale_log2 = (float)(scale * 1.4426950408889634);
+  p->seg = seg_table(L);
+  *kv_end_out = kv_end;
+  return SQG_OK;
+}
+
+// One attention pass of p's query rows over keys [kv_begin, kv_end), in key blocks of
+// kv_block rows merged through the LSE buffer (the first block honours `accumulate`).
+int attn_launch_blocks(sqg::AttnParams p, int64_t kv_begin, int64_t kv_end, int64_t kv_block,
+                       int32_t accumulate, void* stream) {
+  const auto blocks = chunk_plan(kv_end - kv_begin, kv_block, 512);
+  for (size_t i = 0; i < blocks.size(); ++i) {
+    p.kv_begin = kv_begin + blocks[i].first;
+    p.kv_end = kv_begin + blocks[i].second;
+    p.accumulate = (i == 0) ? accumulate : 1;
+    const int st = launch_status(sqg::launch_packed_attention(p, stream), "packed_kv_attention launch");
+    if (st != SQG_OK) return st;
+  }
+  return SQG_OK;
+}
+
+// Default query chunk of the Q-recompute mode: 16384 rows, or more when there are few
+// heads, so that one attention launch still has at least 2048 workgroups (8 per CU).
+int64_t default_q_chunk(int64_t heads) {
+  const int64_t rows = 256 * ((2048 + heads - 1) / heads);
+  return rows > 16384 ? rows : 16384;
+}
+
 }  // namespace
 
 extern "C" {
@@ -153,6 +245,7 @@ SQG_API int64_t sqg_struct_size(int which) {
     case 1: return (int64_t)sizeof(sqg_layout);
     case 2: return (int64_t)sizeof(sqg_qkv_args);
     case 3: return (int64_t)sizeof(sqg_attn_args);
+    case 4: return (int64_t)sizeof(sqg_qrecompute_args);
     default: return -1;
   }
 }
@@ -206,7 +299,10 @@ SQG_API int sqg_streamed_qkv_quant(const sqg_qkv_args* a, void* stream) {
     return fail(SQG_ERR_UNSUPPORTED, "d_model must be a multiple of 256 (got %lld)", (long long)d);
   if (d * a->ldw * 2 > 0x7fffffffLL || 256 * a->ldx * 2 > 0x7fffffffLL)
     return fail(SQG_ERR_UNSUPPORTED, "W (or a 256-row slice of x) exceeds the 2 GiB a buffer resource addresses");
-  if (a->reserved != 0) return fail(SQG_ERR_INVALID_ARGUMENT, "reserved field not 0");
+  if (a->emit != SQG_EMIT_QKV && a->emit != SQG_EMIT_Q && a->emit != SQG_EMIT_KV)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "unknown emit mode %d", a->emit);
+  const bool want_q = a->emit != SQG_EMIT_KV;
+  const bool want_kv = a->emit != SQG_EMIT_Q;
   if ((a->q_norm_w == nullptr) != (a->k_norm_w == nullptr))
     return fail(SQG_ERR_INVALID_ARGUMENT, "q_norm_w and k_norm_w must both be set or both be NULL");
   if ((a->rope_cos == nullptr) != (a->rope_sin == nullptr))
@@ -217,14 +313,18 @@ SQG_API int sqg_streamed_qkv_quant(const sqg_qkv_args* a, void* stream) {
     return fail(SQG_ERR_INVALID_ARGUMENT, "chunk_rows must be 0 or a positive multiple of 128 (got %lld)",
                 (long long)a->chunk_rows);
   if (N == 0) return ok();
-  if (!a->x || !a->w_qkv || !a->q || !a->kpack || !a->vpack || !a->kscale || !a->vscale)
+  if (!a->x || !a->w_qkv || (want_q && !a->q) ||
+      (want_kv && (!a->kpack || !a->vpack || !a->kscale || !a->vscale)))
     return fail(SQG_ERR_INVALID_ARGUMENT, "a required device pointer is NULL");
-  if (a->ldx < d || a->ldw < 3 * d || a->ldq < d)
+  const int64_t ldq = want_q ? a->ldq : d;
+  if (a->ldx < d || a->ldw < 3 * d || ldq < d)
     return fail(SQG_ERR_INVALID_ARGUMENT, "row strides must be >= the row length (ldx %lld, ldw %lld, ldq %lld)",
-                (long long)a->ldx, (long long)a->ldw, (long long)a->ldq);
-  if (a->ldx % 8 || a->ldw % 8 || a->ldq % 8)
+                (long long)a->ldx, (long long)a->ldw, (long long)ldq);
+  if (a->ldx % 8 || a->ldw % 8 || ldq % 8)
     return fail(SQG_ERR_MISALIGNED, "row strides must be multiples of 8 elements");
-  const void* ptrs[] = {a->x, a->w_qkv, a->q, a->kpack, a->vpack, a->kscale, a->vscale,
+  const void* ptrs[] = {a->x, a->w_qkv, want_q ? a->q : nullptr,
+                        want_kv ? a->kpack : nullptr, want_kv ? a->vpack : nullptr,
+                        want_kv ? a->kscale : nullptr, want_kv ? a->vscale : nullptr,
                         a->q_norm_w, a->k_norm_w, a->rope_cos, a->rope_sin};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(SQG_ERR_MISALIGNED, "device pointer %p is not 16-byte aligned", p);
@@ -233,22 +333,25 @@ SQG_API int sqg_streamed_qkv_quant(const sqg_qkv_args* a, void* stream) {
   std::memset(&p, 0, sizeof p);
   p.x = static_cast<const uint16_t*>(a->x);
   p.w = static_cast<const uint16_t*>(a->w_qkv);
-  p.q = static_cast<uint16_t*>(a->q);
-  p.kpack = static_cast<uint8_t*>(a->kpack);
-  p.vpack = static_cast<uint8_t*>(a->vpack);
-  p.kscale = static_cast<uint16_t*>(a->kscale);
-  p.vscale = static_cast<uint16_t*>(a->vscale);
+  p.q = want_q ? static_cast<uint16_t*>(a->q) : nullptr;
+  p.kpack = want_kv ? static_cast<uint8_t*>(a->kpack) : nullptr;
+  p.vpack = want_kv ? static_cast<uint8_t*>(a->vpack) : nullptr;
+  p.kscale = want_kv ? static_cast<uint16_t*>(a->kscale) : nullptr;
+  p.vscale = want_kv ? static_cast<uint16_t*>(a->vscale) : nullptr;
   p.q_norm_w = a->q_norm_w;
   p.k_norm_w = a->k_norm_w;
   p.rope_cos = a->rope_cos;
   p.rope_sin = a->rope_sin;
   p.ldx = a->ldx;
   p.ldw = a->ldw;
-  p.ldq = a->ldq;
+  p.ldq = ldq;
   p.n_tokens = N;
+  p.q_row0 = 0;
   p.d_model = a->d_model;
   p.n_heads = a->n_heads;
   p.eps = a->eps;
+  p.col_tile0 = want_q ? 0 : (int32_t)(d / 256);
+  p.n_col_tiles = (int32_t)((want_q ? d / 256 : 0) + (want_kv ? 2 * d / 256 : 0));
   p.seg = seg_table(L);
   const int64_t min_tail = a->min_tail < 0 ? 512 : a->min_tail;
   for (const auto& c : chunk_plan(N, a->chunk_rows, min_tail)) {
@@ -262,68 +365,101 @@ SQG_API int sqg_streamed_qkv_quant(const sqg_qkv_args* a, void* stream) {
 
 SQG_API int sqg_packed_kv_attention(const sqg_attn_args* a, void* stream) {
   if (!a) return fail(SQG_ERR_INVALID_ARGUMENT, "args is NULL");
-  sqg_layout L;
-  int st = build_layout(a->n_tokens, a->d_model, a->n_heads, a->ranges, a->n_ranges, &L);
-  if (st != SQG_OK) return st;
-  const int64_t N = a->n_tokens;
-  const int64_t d = a->d_model;
-  if (a->o_dtype != SQG_F32 && a->o_dtype != SQG_BF16 && a->o_dtype != SQG_F16)
-    return fail(SQG_ERR_INVALID_ARGUMENT, "unknown o_dtype %d", a->o_dtype);
-  const int64_t q_end = a->q_end == 0 ? N : a->q_end;
-  const int64_t kv_end = a->kv_end == 0 ? N : a->kv_end;
-  if (a->q_begin < 0 || a->q_begin > q_end || q_end > N)
-    return fail(SQG_ERR_INVALID_ARGUMENT, "query range [%lld, %lld) is outside [0, %lld]",
-                (long long)a->q_begin, (long long)q_end, (long long)N);
-  if (a->kv_block < 0 || a->kv_block % 128 != 0)
-    return fail(SQG_ERR_INVALID_ARGUMENT, "kv_block must be 0 or a positive multiple of 128");
-  if (a->accumulate != 0 && a->accumulate != 1)
-    return fail(SQG_ERR_INVALID_ARGUMENT, "accumulate must be 0 or 1");
-  if ((a->accumulate || a->kv_block > 0) && (!a->lse || a->o_dtype != SQG_F32))
-    return fail(SQG_ERR_INVALID_ARGUMENT,
-                "accumulate and kv_block > 0 need an lse buffer and o_dtype SQG_F32");
-  if (!(std::isfinite(a->softmax_scale) && a->softmax_scale >= 0.0f))
-    return fail(SQG_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
-  if (N == 0 || q_end == a->q_begin) return ok();
-  if (a->kv_begin < 0 || a->kv_begin >= kv_end || kv_end > N)
-    return fail(SQG_ERR_INVALID_ARGUMENT, "key range [%lld, %lld) is empty or outside [0, %lld]",
-                (long long)a->kv_begin, (long long)kv_end, (long long)N);
-  if (a->kv_begin % 128 != 0)
-    return fail(SQG_ERR_INVALID_ARGUMENT, "kv_begin must be a multiple of 128");
-  if (!a->q || !a->kpack || !a->vpack || !a->kscale || !a->vscale || !a->o)
-    return fail(SQG_ERR_INVALID_ARGUMENT, "a required device pointer is NULL");
-  if (a->ldq < d || a->ldo < d)
-    return fail(SQG_ERR_INVALID_ARGUMENT, "row strides must be >= d_model");
-  if (a->ldq % 8 || a->ldo % 8) return fail(SQG_ERR_MISALIGNED, "row strides must be multiples of 8");
-  const void* ptrs[] = {a->q, a->kpack, a->vpack, a->kscale, a->vscale, a->o, a->lse};
-  for (const void* p : ptrs)
-    if (p && !aligned16(p)) return fail(SQG_ERR_MISALIGNED, "device pointer %p is not 16-byte aligned", p);
-
   sqg::AttnParams p;
-  std::memset(&p, 0, sizeof p);
-  p.q = static_cast<const uint16_t*>(a->q);
-  p.kpack = static_cast<const uint8_t*>(a->kpack);
-  p.vpack = static_cast<const uint8_t*>(a->vpack);
-  p.kscale = static_cast<const uint16_t*>(a->kscale);
-  p.vscale = static_cast<const uint16_t*>(a->vscale);
-  p.o = a->o;
-  p.lse = a->lse;
-  p.ldq = a->ldq;
-  p.ldo = a->ldo;
-  p.n_tokens = N;
-  p.q_begin = a->q_begin;
-  p.q_end = q_end;
-  p.d_model = a->d_model;
-  p.n_heads = a->n_heads;
-  p.o_dtype = a->o_dtype;
-  const double scale = a->softmax_scale > 0.0f ? (double)a->softmax_scale : 1.0 / std::sqrt(128.0);
-  p.scale_log2 = (float)(scale * 1.4426950408889634);
-  p.seg = seg_table(L);
-  const auto blocks = chunk_plan(kv_end - a->kv_begin, a->kv_block, 512);
-  for (size_t i = 0; i < blocks.size(); ++i) {
-    p.kv_begin = a->kv_begin + blocks[i].first;
-    p.kv_end = a->kv_begin + blocks[i].second;
-    p.accumulate = (i == 0) ? a->accumulate : 1;
-    st = launch_status(sqg::launch_packed_attention(p, stream), "packed_kv_attention launch");
+  int64_t kv_end = 0;
+  bool empty = false;
+  int st = attn_prepare(a, true, &p, &kv_end, &empty);
+  if (st != SQG_OK) return st;
+  if (empty) return ok();
+  st = attn_launch_blocks(p, a->kv_begin, kv_end, a->kv_block, a->accumulate, stream);
+  return st == SQG_OK ? ok() : st;
+}
+
+SQG_API int64_t sqg_qrecompute_workspace_bytes(int64_t n_query_rows, int64_t q_chunk_rows,
+                                               int32_t d_model) {
+  if (n_query_rows < 0 || q_chunk_rows < 0 || q_chunk_rows % 128 != 0 || d_model <= 0 ||
+      d_model % SQG_HEAD_DIM != 0)
+    return -1;
+  const int64_t size = q_chunk_rows == 0 ? default_q_chunk(d_model / SQG_HEAD_DIM) : q_chunk_rows;
+  int64_t rows = 0;
+  for (const auto& c : chunk_plan(n_query_rows, size, 512))
+    rows = c.second - c.first > rows ? c.second - c.first : rows;
+  return rows * d_model * 2;
+}
+
+SQG_API int sqg_packed_kv_attention_qrecompute(const sqg_qrecompute_args* a, void* stream) {
+  if (!a) return fail(SQG_ERR_INVALID_ARGUMENT, "args is NULL");
+  const sqg_attn_args& at = a->attn;
+  sqg::AttnParams ap;
+  int64_t kv_end = 0;
+  bool empty = false;
+  int st = attn_prepare(&at, false, &ap, &kv_end, &empty);
+  if (st != SQG_OK) return st;
+  const int64_t d = at.d_model;
+  if (d % 256 != 0)
+    return fail(SQG_ERR_UNSUPPORTED, "d_model must be a multiple of 256 (got %lld)", (long long)d);
+  if (a->reserved != 0) return fail(SQG_ERR_INVALID_ARGUMENT, "reserved field not 0");
+  if (a->q_chunk_rows < 0 || a->q_chunk_rows % 128 != 0)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "q_chunk_rows must be 0 or a positive multiple of 128 (got %lld)",
+                (long long)a->q_chunk_rows);
+  if ((a->rope_cos == nullptr) != (a->rope_sin == nullptr))
+    return fail(SQG_ERR_INVALID_ARGUMENT, "rope_cos and rope_sin must both be set or both be NULL");
+  if (a->q_norm_w && !(a->eps >= 0.0f && std::isfinite(a->eps)))
+    return fail(SQG_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if (empty) return ok();
+  const int64_t n_q = ap.q_end - ap.q_begin;
+  const int64_t need = sqg_qrecompute_workspace_bytes(n_q, a->q_chunk_rows, at.d_model);
+  if (!a->x || !a->w_qkv || !a->workspace)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "a required device pointer is NULL");
+  if (a->workspace_bytes < need)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "workspace holds %lld bytes, %lld needed",
+                (long long)a->workspace_bytes, (long long)need);
+  if (a->ldx < d || a->ldw < 3 * d)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "row strides must be >= the row length (ldx %lld, ldw %lld)",
+                (long long)a->ldx, (long long)a->ldw);
+  if (a->ldx % 8 || a->ldw % 8) return fail(SQG_ERR_MISALIGNED, "row strides must be multiples of 8 elements");
+  if (d * a->ldw * 2 > 0x7fffffffLL || 256 * a->ldx * 2 > 0x7fffffffLL)
+    return fail(SQG_ERR_UNSUPPORTED, "W (or a 256-row slice of x) exceeds the 2 GiB a buffer resource addresses");
+  const void* ptrs[] = {a->x, a->w_qkv, a->workspace, a->q_norm_w, a->rope_cos, a->rope_sin};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(SQG_ERR_MISALIGNED, "device pointer %p is not 16-byte aligned", ptr);
+
+  // Q-only projection of one chunk into the workspace (row t at row t - chunk start)
+  sqg::QkvParams qp;
+  std::memset(&qp, 0, sizeof qp);
+  qp.x = static_cast<const uint16_t*>(a->x);
+  qp.w = static_cast<const uint16_t*>(a->w_qkv);
+  qp.q = static_cast<uint16_t*>(a->workspace);
+  qp.q_norm_w = a->q_norm_w;
+  qp.rope_cos = a->rope_cos;
+  qp.rope_sin = a->rope_sin;
+  qp.ldx = a->ldx;
+  qp.ldw = a->ldw;
+  qp.ldq = d;
+  qp.n_tokens = at.n_tokens;
+  qp.d_model = at.d_model;
+  qp.n_heads = at.n_heads;
+  qp.eps = a->eps;
+  qp.col_tile0 = 0;
+  qp.n_col_tiles = (int32_t)(d / 256);
+  qp.seg = ap.seg;
+
+  ap.q = static_cast<const uint16_t*>(a->workspace);
+  ap.ldq = d;
+  const int64_t size = a->q_chunk_rows == 0 ? default_q_chunk(at.n_heads) : a->q_chunk_rows;
+  for (const auto& c : chunk_plan(n_q, size, 512)) {
+    const int64_t c0 = ap.q_begin + c.first;  // chunk offsets are relative to the range start
+    const int64_t c1 = ap.q_begin + c.second;
+    qp.row_begin = c0;
+    qp.row_end = c1;
+    qp.q_row0 = c0;
+    st = launch_status(sqg::launch_qkv_quant(qp, stream), "q recompute launch");
+    if (st != SQG_OK) return st;
+    sqg::AttnParams cp = ap;
+    cp.q_begin = c0;
+    cp.q_end = c1;
+    cp.q_row0 = c0;
+    st = attn_launch_blocks(cp, at.kv_begin, kv_end, at.kv_block, at.accumulate, stream);
     if (st != SQG_OK) return st;
   }
   return ok();

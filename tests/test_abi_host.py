@@ -39,6 +39,7 @@ def test_struct_sizes_match_binding():
     assert lib.sqg_struct_size(1) == ctypes.sizeof(B.Layout)
     assert lib.sqg_struct_size(2) == ctypes.sizeof(B.QkvArgs)
     assert lib.sqg_struct_size(3) == ctypes.sizeof(B.AttnArgs)
+    assert lib.sqg_struct_size(4) == ctypes.sizeof(B.QRecomputeArgs)
     assert lib.sqg_struct_size(9) == -1
 
 
@@ -148,13 +149,88 @@ def attn_args(**kw):
     (dict(x=None), -1),
     (dict(q_norm_w=FAKE), -1),                     # q norm without k norm
     (dict(rope_cos=FAKE), -1),                     # cos without sin
-    (dict(reserved=1), -1),
+    (dict(emit=3), -1),                            # unknown emit mode
+    (dict(emit=1, q=None), -1),                    # Q only needs q
+    (dict(emit=2, kscale=None), -1),               # K/V only needs the store
 ])
 def test_qkv_argument_errors(kw, status):
     lib = sqg.load()
     a = qkv_args(**kw)
     assert lib.sqg_streamed_qkv_quant(ctypes.byref(a), None) == status
     assert len(lib.sqg_last_error()) > 0
+
+
+def test_qkv_emit_modes_drop_the_unused_pointers():
+    """Q only needs no store pointers, K/V only needs no q: a later check fires instead."""
+    lib = sqg.load()
+    a = qkv_args(emit=1, kpack=None, vpack=None, kscale=None, vscale=None, ldx=500)
+    assert lib.sqg_streamed_qkv_quant(ctypes.byref(a), None) == -1
+    assert b"row strides" in lib.sqg_last_error()
+    a = qkv_args(emit=2, q=None, ldq=0, x=FAKE + 8)
+    assert lib.sqg_streamed_qkv_quant(ctypes.byref(a), None) == -3
+    assert b"aligned" in lib.sqg_last_error()
+
+
+def qrec_args(**kw):
+    r = B.QRecomputeArgs()
+    r.attn = attn_args(q=None, ldq=0)
+    r.x, r.ldx, r.w_qkv, r.ldw = FAKE, 512, FAKE, 1536
+    r.eps, r.q_chunk_rows = 1e-6, 0
+    r.workspace, r.workspace_bytes = FAKE, 1024 * 512 * 2
+    for k, v in kw.items():
+        if k.startswith("attn_"):
+            setattr(r.attn, k[5:], v)
+        else:
+            setattr(r, k, v)
+    return r
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(workspace_bytes=1024 * 512 * 2 - 2), -1, b"workspace"),
+    (dict(q_chunk_rows=256, workspace_bytes=256 * 512 * 2 - 2), -1, b"workspace"),
+    (dict(workspace=None), -1, b"NULL"),
+    (dict(x=None), -1, b"NULL"),
+    (dict(reserved=1), -1, b"reserved"),
+    (dict(q_chunk_rows=100), -1, b"q_chunk_rows"),
+    (dict(q_chunk_rows=-128), -1, b"q_chunk_rows"),
+    (dict(rope_cos=FAKE), -1, b"rope_sin"),
+    (dict(ldx=500), -1, b"row strides"),
+    (dict(ldw=1000), -1, b"row strides"),
+    (dict(x=FAKE + 8), -3, b"aligned"),
+    (dict(workspace=FAKE + 8), -3, b"aligned"),
+    (dict(attn_d_model=384, attn_n_heads=3), -2, b"multiple of 256"),
+    (dict(attn_kv_begin=64), -1, b"kv_begin"),
+    (dict(attn_kpack=None), -1, b"NULL"),
+    (dict(attn_accumulate=1, attn_lse=None), -1, b"lse"),
+])
+def test_qrecompute_argument_errors(kw, status, msg):
+    lib = sqg.load()
+    r = qrec_args(**kw)
+    assert lib.sqg_packed_kv_attention_qrecompute(ctypes.byref(r), None) == status
+    assert msg in lib.sqg_last_error()
+
+
+def test_qrecompute_empty_query_range_is_a_noop():
+    lib = sqg.load()
+    r = qrec_args(attn_q_begin=300, attn_q_end=300, workspace=None, workspace_bytes=0)
+    assert lib.sqg_packed_kv_attention_qrecompute(ctypes.byref(r), None) == 0
+
+
+@pytest.mark.parametrize("n,chunk,d,want", [
+    (1000, 0, 512, 1000 * 1024),                   # one chunk
+    (300000, 0, 512, 131072 * 1024),               # 4 heads: default chunk 256 * 512 rows
+    (131584, 0, 512, 131072 * 1024),               # 512-row tail stays a chunk of its own...
+    (131583, 0, 512, 131583 * 1024),               # ...511 rows join the chunk before it
+    (217088, 0, 7168, 16384 * 14336),              # 56 heads: default chunk 16384 rows
+    (1000, 256, 384, 488 * 768),                   # 232-row tail joins the chunk at 512
+    (1200, 512, 384, 688 * 768),                   # 176-row tail joins the second chunk
+    (0, 0, 512, 0),
+    (-1, 0, 512, -1),
+    (1000, 100, 512, -1),
+    (1000, 0, 0, -1),
+])
+def test_qrecompute_workspace_bytes(n, chunk, d, want):
+    assert sqg.load().sqg_qrecompute_workspace_bytes(n, chunk, d) == want
 
 
 def test_qkv_bad_policy_rejected():
