@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--qrecompute-steps", type=int, default=1,
                     help="steps of the Q-recompute variant timed after the main steps (0 = skip)")
     ap.add_argument("--q-chunk-rows", type=int, default=0, help="query chunk of the Q-recompute variant")
+    ap.add_argument("--staged-steps", type=int, default=1,
+                    help="steps of the host-staged K/V variant timed after the main steps (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, copy this many MiB device-to-device three times "
                          "(reference dispatches for HBM byte counters)")
@@ -178,6 +180,43 @@ def main():
         del kv_store, ws
         torch.cuda.empty_cache()
 
+    # ---- host-staged variant: the packed K/V lives in pinned host memory, one block of
+    # kv_block keys at a time on the GPU (timed separately, not part of value)
+    staged_res = None
+    if args.staged_steps > 0:
+        block = wl.kv_block if wl.kv_block > 0 else 16384
+        stg = sqg.alloc_staged(N, d, block, wl.ranges, device=dev)
+        q_st = torch.empty((N, d), dtype=torch.bfloat16, device=dev)
+
+        def staged_step(ev=None):
+            if ev:
+                ev[0].record(stream)
+            sqg.streamed_qkv_quant_staged(x, w, stg, q=q_st, **kw)
+            if ev:
+                ev[1].record(stream)
+            sqg.packed_kv_attention_staged(stg, q_st, o=o, lse=lse)
+            if ev:
+                ev[2].record(stream)
+
+        staged_step()
+        torch.cuda.synchronize()
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.staged_steps)]
+        for i in range(args.staged_steps):
+            staged_step(sev[i])
+        torch.cuda.synchronize()
+        b_ms = sum(e[0].elapsed_time(e[1]) for e in sev) / args.staged_steps
+        a_ms = sum(e[1].elapsed_time(e[2]) for e in sev) / args.staged_steps
+        (hp, hs, dp, ds), nb = sqg.staged_sizes(N, d, block, wl.ranges)
+        staged_res = {"steps": args.staged_steps, "block_rows": block, "n_blocks": nb,
+                      "ms_per_step": b_ms + a_ms,
+                      "tflops": (qkv_flop + att_flop) / ((b_ms + a_ms) * 1e-3) / 1e12,
+                      "qkv_quant_to_host_ms": b_ms, "attention_from_host_ms": a_ms,
+                      "host_store_bytes": 2 * (hp + hs), "device_staging_bytes": 4 * (dp + ds),
+                      "device_kv_bytes_vs_device_store": 4 * (dp + ds) / (2 * (hp + hs)),
+                      "copies": "synchronous order on the compute stream (no copy/compute overlap)"}
+        del stg, q_st
+        torch.cuda.empty_cache()
+
     # ---- bf16-materialising baseline: x @ W into a bf16 [N, 3d] tensor (library GEMM)
     bf16_base = None
     if not args.no_bf16_baseline:
@@ -231,6 +270,7 @@ def main():
         "working_set_ratio": packed_ws / L["bf16_qkv_bytes"],
         "bf16_materialising_baseline": bf16_base,
         "qrecompute": qrec,
+        "host_staged": staged_res,
         "wall_s_timed": wall,
         "roofline": {
             "kernel": "packed_attention_kernel",

@@ -36,7 +36,7 @@ extern "C" {
 #define SQG_API
 #endif
 
-#define SQG_VERSION 100          /* 1.0.0 */
+#define SQG_VERSION 110          /* 1.1.0 */
 #define SQG_HEAD_DIM 128
 #define SQG_GROUP 32
 #define SQG_MAX_SEGMENTS 16
@@ -83,7 +83,10 @@ typedef struct sqg_range {
  * codes of (head h, token t) start at byte
  *   seg_offset[s] + (h * (seg_end[s] - seg_begin[s]) + (t - seg_begin[s])) * seg_row_bytes[s]
  * of the kpack (vpack) buffer, where seg_row_bytes is 64 for INT4 and 128 for INT8.
- * Scales are fp16 [n_heads, n_tokens, 4]: group g of (h, t) at element (h*N + t)*4 + g. */
+ * Scales are fp16 [n_heads, n_tokens, 4]: group g of (h, t) at element (h*N + t)*4 + g.
+ * A block store (sqg_kv_block_layout) holds only keys [k0, k1): n_tokens = k1 - k0, the
+ * segments are the policy's clipped to [k0, k1) (seg_begin/seg_end stay absolute token
+ * indices, seg_begin[0] = k0), and token t's scales sit at row t - k0. */
 typedef struct sqg_layout {
   int64_t n_tokens;
   int32_t n_heads;
@@ -152,6 +155,26 @@ typedef struct sqg_attn_args {
                                   required when accumulate or kv_block > 0 */
 } sqg_attn_args;
 
+/* A K/V store held in host memory as consecutive block stores ([VL] module docstring:
+ * the host-staged ("turtle") K/V the pages name as the real fix for the K/V peak).
+ * Keys are split into blocks of block_rows (sqg_chunk_ranges(N, block_rows, 512):
+ * a last block shorter than 512 keys joins the previous one).  Block b is a block store
+ * (sqg_kv_block_layout) whose codes start at host_kpack + (sum of the pack_bytes of
+ * blocks before b), and whose scales start at host_kscale + (sum of their scale_bytes);
+ * likewise for V.  Two device staging block stores carry blocks between host and
+ * kernels.  sqg_staged_sizes gives every buffer size. */
+typedef struct sqg_staged_kv {
+  int64_t block_rows;          /* keys per block, a positive multiple of 128 */
+  void* host_kpack;            /* pinned host (hipHostMalloc / pinned torch tensors) */
+  void* host_vpack;
+  void* host_kscale;
+  void* host_vscale;
+  void* dev_kpack[2];          /* device staging */
+  void* dev_vpack[2];
+  void* dev_kscale[2];
+  void* dev_vscale[2];
+} sqg_staged_kv;
+
 /* Arguments of sqg_packed_kv_attention_qrecompute. */
 typedef struct sqg_qrecompute_args {
   sqg_attn_args attn;          /* as for sqg_packed_kv_attention, except that attn.q and attn.ldq
@@ -184,7 +207,7 @@ SQG_API const char* sqg_last_error(void);
 
 /* sizeof of the argument structs, so bindings can check their mirrors:
  * which = 0 sqg_range, 1 sqg_layout, 2 sqg_qkv_args, 3 sqg_attn_args,
- * 4 sqg_qrecompute_args; else -1. */
+ * 4 sqg_qrecompute_args, 5 sqg_staged_kv; else -1. */
 SQG_API int64_t sqg_struct_size(int which);
 
 /* Host only.  Row chunks of `size` rows over [0, n); a last chunk shorter than
@@ -201,6 +224,22 @@ SQG_API int sqg_chunk_ranges(int64_t n, int64_t size, int64_t min_tail, int64_t*
  * d_model must be 128 * n_heads. */
 SQG_API int sqg_kv_layout(int64_t n_tokens, int32_t d_model, int32_t n_heads,
                           const sqg_range* ranges, int32_t n_ranges, sqg_layout* out);
+
+/* Host only.  Layout of the block store that holds keys [key_begin, key_end) of the
+ * sequence the policy describes (see sqg_layout).  key_begin must be a multiple of 128
+ * and 0 <= key_begin < key_end <= n_tokens. */
+SQG_API int sqg_kv_block_layout(int64_t n_tokens, int32_t d_model, int32_t n_heads,
+                                const sqg_range* ranges, int32_t n_ranges, int64_t key_begin,
+                                int64_t key_end, sqg_layout* out);
+
+/* Host only.  Buffer sizes of a host-staged store with blocks of block_rows keys:
+ * sizes[0] = bytes of host_kpack (and of host_vpack), sizes[1] = bytes of host_kscale
+ * (and host_vscale), sizes[2] = bytes of each dev_kpack / dev_vpack staging buffer (the
+ * largest block), sizes[3] = bytes of each dev_kscale / dev_vscale staging buffer;
+ * *n_blocks = the number of blocks. */
+SQG_API int sqg_staged_sizes(int64_t n_tokens, int32_t d_model, int32_t n_heads,
+                             const sqg_range* ranges, int32_t n_ranges, int64_t block_rows,
+                             int64_t sizes[4], int32_t* n_blocks);
 
 /* Host only.  Split-half RoPE tables for positions [pos0, pos0 + n): cos and sin of
  * pos * theta^(-2i/128), i in [0, 64), computed in fp64 and rounded to fp32, into the
@@ -251,6 +290,28 @@ SQG_API int64_t sqg_qrecompute_workspace_bytes(int64_t n_query_rows, int64_t q_c
  * plus one chunk of Q.  Results equal sqg_streamed_qkv_quant (SQG_EMIT_Q) followed by
  * sqg_packed_kv_attention bit for bit. */
 SQG_API int sqg_packed_kv_attention_qrecompute(const sqg_qrecompute_args* args, void* stream);
+
+/* sqg_streamed_qkv_quant with the packed K/V kept in host memory: for each key block,
+ * the kernel writes the block's K/V into a device staging block store (alternating
+ * between the two) and an asynchronous copy moves it to the block's place in the host
+ * store.  args->kpack, vpack, kscale and vscale are ignored; Q (unless emit is
+ * SQG_EMIT_KV) goes to args->q as usual; chunk_rows and min_tail are ignored (each block
+ * is one launch).  Every copy and launch is enqueued on `stream`, in order; the host
+ * store is complete once the stream has reached the end of the call.  emit
+ * SQG_EMIT_Q is rejected (there is no K/V to stage). */
+SQG_API int sqg_streamed_qkv_quant_staged(const sqg_qkv_args* args, const sqg_staged_kv* staged,
+                                          void* stream);
+
+/* sqg_packed_kv_attention against a host-staged store: for each block that meets
+ * [kv_begin, kv_end), an asynchronous copy brings the block into a device staging
+ * block store and the attention kernel processes its keys, merged into (O, LSE)
+ * through the log-sum-exp ([VL] kvi8r section, `_online_combine`).  The blocks take
+ * the place of kv_block (args->kv_block is ignored), so with more than one block an
+ * lse buffer and SQG_F32 output are required.  args->kpack, vpack, kscale, vscale are
+ * ignored.  Results equal sqg_packed_kv_attention on the device store with kv_block =
+ * block_rows bit for bit.  The device never holds more than two blocks of K/V. */
+SQG_API int sqg_packed_kv_attention_staged(const sqg_attn_args* args, const sqg_staged_kv* staged,
+                                           void* stream);
 
 /* Test entry: runs the kernels' own quantise-and-pack step on fp32 rotated vectors
  * r (device, [rows, 128]) with format fmt for every row; writes codes (device,

@@ -67,6 +67,12 @@ class AttnArgs(ctypes.Structure):
                 ("o", _vp), ("ldo", _c_i64), ("lse", _vp)]
 
 
+class StagedKV(ctypes.Structure):
+    _fields_ = [("block_rows", _c_i64), ("host_kpack", _vp), ("host_vpack", _vp),
+                ("host_kscale", _vp), ("host_vscale", _vp), ("dev_kpack", _vp * 2),
+                ("dev_vpack", _vp * 2), ("dev_kscale", _vp * 2), ("dev_vscale", _vp * 2)]
+
+
 class QRecomputeArgs(ctypes.Structure):
     _fields_ = [("attn", AttnArgs), ("x", _vp), ("ldx", _c_i64), ("w_qkv", _vp), ("ldw", _c_i64),
                 ("q_norm_w", _vp), ("rope_cos", _vp), ("rope_sin", _vp), ("eps", ctypes.c_float),
@@ -100,12 +106,19 @@ def load(path: Optional[str] = None):
     lib.sqg_rope_table.argtypes = [_c_i64, _c_i64, ctypes.c_double, _vp, _vp]
     lib.sqg_streamed_qkv_quant.argtypes = [ctypes.POINTER(QkvArgs), _vp]
     lib.sqg_packed_kv_attention.argtypes = [ctypes.POINTER(AttnArgs), _vp]
+    lib.sqg_kv_block_layout.argtypes = [_c_i64, _c_i32, _c_i32, ctypes.POINTER(Range), _c_i32,
+                                        _c_i64, _c_i64, ctypes.POINTER(Layout)]
+    lib.sqg_staged_sizes.argtypes = [_c_i64, _c_i32, _c_i32, ctypes.POINTER(Range), _c_i32, _c_i64,
+                                     ctypes.POINTER(_c_i64), ctypes.POINTER(_c_i32)]
+    lib.sqg_streamed_qkv_quant_staged.argtypes = [ctypes.POINTER(QkvArgs), ctypes.POINTER(StagedKV), _vp]
+    lib.sqg_packed_kv_attention_staged.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(StagedKV), _vp]
     lib.sqg_qrecompute_workspace_bytes.restype = _c_i64
     lib.sqg_qrecompute_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i32]
     lib.sqg_packed_kv_attention_qrecompute.argtypes = [ctypes.POINTER(QRecomputeArgs), _vp]
     lib.sqg_test_quant_pack_f32.argtypes = [_vp, _c_i64, _c_i32, _vp, _vp, _vp]
     lib.sqg_test_fwht_f32.argtypes = [_vp, _vp, _c_i64, _c_i32, _vp]
-    for name, cls in ((0, Range), (1, Layout), (2, QkvArgs), (3, AttnArgs), (4, QRecomputeArgs)):
+    for name, cls in ((0, Range), (1, Layout), (2, QkvArgs), (3, AttnArgs), (4, QRecomputeArgs),
+                      (5, StagedKV)):
         got = lib.sqg_struct_size(name)
         if got != ctypes.sizeof(cls):
             raise RuntimeError("ABI mismatch: %s is %d bytes in the library, %d in the binding"
@@ -160,16 +173,30 @@ def chunk_ranges(n: int, size: int, min_tail: int = 512):
     return [(b[i], e[i]) for i in range(count.value)]
 
 
-def kv_layout(n_tokens: int, d_model: int, ranges=None) -> Dict:
-    lib = load()
-    arr, nr = _ranges_array(ranges)
-    L = Layout()
-    _check(lib.sqg_kv_layout(n_tokens, d_model, d_model // HEAD_DIM, arr, nr, ctypes.byref(L)))
+def _layout_dict(L) -> Dict:
     segs = [{"begin": L.seg_begin[i], "end": L.seg_end[i], "fmt": L.seg_fmt[i],
              "offset": L.seg_offset[i], "row_bytes": L.seg_row_bytes[i]} for i in range(L.n_segments)]
     return {"n_tokens": L.n_tokens, "n_heads": L.n_heads, "segments": segs,
             "q_bytes": L.q_bytes, "pack_bytes": L.pack_bytes, "scale_bytes": L.scale_bytes,
             "bf16_qkv_bytes": L.bf16_qkv_bytes}
+
+
+def kv_block_layout(n_tokens: int, d_model: int, key_begin: int, key_end: int, ranges=None) -> Dict:
+    """Layout of the block store that holds keys [key_begin, key_end)."""
+    lib = load()
+    arr, nr = _ranges_array(ranges)
+    L = Layout()
+    _check(lib.sqg_kv_block_layout(n_tokens, d_model, d_model // HEAD_DIM, arr, nr, key_begin,
+                                   key_end, ctypes.byref(L)))
+    return _layout_dict(L)
+
+
+def kv_layout(n_tokens: int, d_model: int, ranges=None) -> Dict:
+    lib = load()
+    arr, nr = _ranges_array(ranges)
+    L = Layout()
+    _check(lib.sqg_kv_layout(n_tokens, d_model, d_model // HEAD_DIM, arr, nr, ctypes.byref(L)))
+    return _layout_dict(L)
 
 
 def rope_table(n_tokens: int, theta: float = 10000.0, pos0: int = 0, device="cuda"):
@@ -330,6 +357,104 @@ def packed_kv_attention_qrecompute(store: Dict, x: torch.Tensor, w_qkv: torch.Te
     r.workspace_bytes = workspace.numel() * workspace.element_size()
     _check(lib.sqg_packed_kv_attention_qrecompute(ctypes.byref(r), _stream(x.device)))
     return o, lse
+
+
+def staged_sizes(n_tokens: int, d_model: int, block_rows: int, ranges=None):
+    """(host pack bytes, host scale bytes, staging pack bytes, staging scale bytes), n_blocks."""
+    lib = load()
+    arr, nr = _ranges_array(ranges)
+    sizes = (_c_i64 * 4)()
+    nb = _c_i32(0)
+    _check(lib.sqg_staged_sizes(n_tokens, d_model, d_model // HEAD_DIM, arr, nr, block_rows, sizes,
+                                ctypes.byref(nb)))
+    return tuple(sizes), nb.value
+
+
+def alloc_staged(n_tokens: int, d_model: int, block_rows: int, ranges=None, device="cuda") -> Dict:
+    """A host-staged K/V store: pinned host buffers for every block, two device staging
+    block stores, and the block plan."""
+    (hp, hs, dp, ds), nb = staged_sizes(n_tokens, d_model, block_rows, ranges)
+    pinned = lambda n: torch.empty((max(n, 16),), dtype=torch.uint8, pin_memory=True)  # noqa: E731
+    dev = lambda n: torch.empty((max(n, 16),), dtype=torch.uint8, device=device)  # noqa: E731
+    st = {"block_rows": block_rows, "n_blocks": nb, "ranges": list(ranges) if ranges else None,
+          "n_tokens": n_tokens, "d_model": d_model,
+          "host_kpack": pinned(hp), "host_vpack": pinned(hp), "host_kscale": pinned(hs),
+          "host_vscale": pinned(hs),
+          "dev_kpack": [dev(dp), dev(dp)], "dev_vpack": [dev(dp), dev(dp)],
+          "dev_kscale": [dev(ds), dev(ds)], "dev_vscale": [dev(ds), dev(ds)]}
+    return st
+
+
+def _staged_struct(st: Dict) -> StagedKV:
+    s = StagedKV()
+    s.block_rows = st["block_rows"]
+    for k in ("host_kpack", "host_vpack", "host_kscale", "host_vscale"):
+        t = st[k]
+        if not t.is_pinned():
+            raise ValueError("%s must be pinned host memory" % k)
+        setattr(s, k, t.data_ptr())
+    for k in ("dev_kpack", "dev_vpack", "dev_kscale", "dev_vscale"):
+        arr = getattr(s, k)
+        for i in range(2):
+            arr[i] = _dev_ptr(st[k][i], k)
+    return s
+
+
+def streamed_qkv_quant_staged(x: torch.Tensor, w_qkv: torch.Tensor, staged: Dict,
+                              q: Optional[torch.Tensor] = None, emit: int = SQG_EMIT_QKV,
+                              q_norm_w: Optional[torch.Tensor] = None,
+                              k_norm_w: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                              rope_cos: Optional[torch.Tensor] = None,
+                              rope_sin: Optional[torch.Tensor] = None):
+    """streamed_qkv_quant with the packed K/V written block by block into the host store
+    `staged` (alloc_staged).  Returns Q (None with emit SQG_EMIT_KV)."""
+    lib = load()
+    N, d = x.shape
+    for t, nm in ((x, "x"), (w_qkv, "w_qkv")):
+        if t.dtype != torch.bfloat16 or t.stride(-1) != 1:
+            raise ValueError("%s must be a row-major bf16 tensor" % nm)
+    if q is None and emit != SQG_EMIT_KV:
+        q = torch.empty((N, d), dtype=torch.bfloat16, device=x.device)
+    arr, nr = _ranges_array(staged.get("ranges"))
+    a = QkvArgs()
+    a.n_tokens, a.d_model, a.n_heads = N, d, d // HEAD_DIM
+    a.x, a.ldx = _dev_ptr(x, "x"), x.stride(0)
+    a.w_qkv, a.ldw = _dev_ptr(w_qkv, "w_qkv"), w_qkv.stride(0)
+    a.q_norm_w, a.k_norm_w = _dev_ptr(q_norm_w, "q_norm_w"), _dev_ptr(k_norm_w, "k_norm_w")
+    a.eps = eps
+    a.rope_cos, a.rope_sin = _dev_ptr(rope_cos, "rope_cos"), _dev_ptr(rope_sin, "rope_sin")
+    a.ranges = ctypes.cast(arr, ctypes.POINTER(Range)) if arr is not None else None
+    a.n_ranges, a.emit = nr, emit
+    if q is not None:
+        a.q, a.ldq = _dev_ptr(q, "q"), q.stride(0)
+    s = _staged_struct(staged)
+    _check(lib.sqg_streamed_qkv_quant_staged(ctypes.byref(a), ctypes.byref(s), _stream(x.device)))
+    return q
+
+
+def packed_kv_attention_staged(staged: Dict, q: torch.Tensor, q_begin: int = 0, q_end: int = 0,
+                               kv_begin: int = 0, kv_end: int = 0, accumulate: bool = False,
+                               o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                               o_dtype=torch.float32, softmax_scale: float = 0.0,
+                               want_lse: bool = True):
+    """packed_kv_attention against the host-staged store: blocks are copied in one at a
+    time and merged through the LSE.  -> (O, lse)."""
+    lib = load()
+    N, d = q.shape
+    a, _keep, o, lse = _attn_args(staged_view(staged), N, d, q.device, q_begin, q_end, kv_begin,
+                                  kv_end, 0, accumulate, o, lse, o_dtype, softmax_scale,
+                                  want_lse or staged["n_blocks"] > 1)
+    a.q, a.ldq = _dev_ptr(q, "q"), q.stride(0)
+    s = _staged_struct(staged)
+    _check(lib.sqg_packed_kv_attention_staged(ctypes.byref(a), ctypes.byref(s), _stream(q.device)))
+    return o, lse
+
+
+def staged_view(staged: Dict) -> Dict:
+    """Store-shaped view for argument marshalling (the store pointers are ignored)."""
+    return {"kpack": staged["dev_kpack"][0], "vpack": staged["dev_vpack"][0],
+            "kscale": staged["dev_kscale"][0], "vscale": staged["dev_vscale"][0],
+            "ranges": staged.get("ranges")}
 
 
 def test_quant_pack_f32(r: torch.Tensor, fmt: int):

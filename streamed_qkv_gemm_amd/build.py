@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsqg.so")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["qkv_quant.hip", "packed_attention.hip", "test_kernels.hip"]
+HIP_SOURCES = ["qkv_quant.hip", "packed_attention.hip", "test_kernels.hip", "runtime.hip"]
 HOST_SOURCES = ["sqg_api.cpp"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in generated code.

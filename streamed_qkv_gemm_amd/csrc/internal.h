@@ -25,7 +25,7 @@ struct QkvParams {
   uint16_t* q;             // bf16 [N, ldq]
   uint8_t* kpack;
   uint8_t* vpack;
-  uint16_t* kscale;        // fp16 [H, N, 4]
+  uint16_t* kscale;        // fp16 [H, kv_n, 4]
   uint16_t* vscale;
   const float* q_norm_w;   // [128] or null
   const float* k_norm_w;
@@ -35,6 +35,7 @@ struct QkvParams {
   int64_t n_tokens;
   int64_t row_begin, row_end;
   int64_t q_row0;          // token t's Q goes to row t - q_row0 of q
+  int64_t kv_row0, kv_n;   // the K/V store holds tokens [kv_row0, kv_row0 + kv_n)
   int32_t d_model, n_heads;
   float eps;
   int32_t col_tile0;       // first 256-column tile of [q | k | v] this launch covers
@@ -49,7 +50,7 @@ struct AttnParams {
   const uint16_t* q;       // bf16 [N, ldq]
   const uint8_t* kpack;
   const uint8_t* vpack;
-  const uint16_t* kscale;  // fp16 [H, N, 4]
+  const uint16_t* kscale;  // fp16 [H, kv_n, 4]
   const uint16_t* vscale;
   void* o;                 // [N, ldo] of o_dtype
   float* lse;              // [H, N] or null
@@ -57,6 +58,7 @@ struct AttnParams {
   int64_t n_tokens;
   int64_t q_begin, q_end;
   int64_t q_row0;          // query row r is row r - q_row0 of q
+  int64_t kv_row0, kv_n;   // the K/V store holds keys [kv_row0, kv_row0 + kv_n)
   int64_t kv_begin, kv_end;
   int32_t d_model, n_heads;
   int32_t o_dtype;
@@ -72,5 +74,9 @@ int launch_test_quant_pack(const float* r, int64_t rows, int32_t fmt, void* code
                            void* stream);
 int launch_test_fwht(const float* in, float* out, int64_t rows, int32_t normalize, void* stream);
 const char* hip_error_text(int err);
+
+// Asynchronous copy on `stream` (hipMemcpyAsync); returns a hipError_t value.
+enum CopyKind { kHostToDevice = 1, kDeviceToHost = 2 };
+int copy_async(void* dst, const void* src, int64_t bytes, CopyKind kind, void* stream);
 
 }  // namespace sqg

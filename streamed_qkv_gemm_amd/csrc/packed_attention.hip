@@ -188,9 +188,9 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
   // zero.  The load cursor below follows the segment of the next tile to load in
   // scalar registers, so a tile costs a few scalar adds and one vector add per base.
   const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.kscale + (int64_t)head * N * 4), 0, (int32_t)(N * 8), kBufferWord3);
+      (void*)(p.kscale + (int64_t)head * p.kv_n * 4), 0, (int32_t)(p.kv_n * 8), kBufferWord3);
   const __amdgpu_buffer_rsrc_t vsr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.vscale + (int64_t)head * N * 4), 0, (int32_t)(N * 8), kBufferWord3);
+      (void*)(p.vscale + (int64_t)head * p.kv_n * 4), 0, (int32_t)(p.kv_n * 8), kBufferWord3);
   int ld_seg = -1;
   int64_t ld_sb = 0, ld_se = 0;
   int ld_fmt = FMT_INT4;
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
       kr = __builtin_amdgcn_make_buffer_rsrc((void*)(p.kpack + base), 0, bytes, kBufferWord3);
       vr = __builtin_amdgcn_make_buffer_rsrc((void*)(p.vpack + base), 0, bytes, kBufferWord3);
     }
-    const uint32_t srow = (uint32_t)(key0 * 8);
+    const uint32_t srow = (uint32_t)((key0 - p.kv_row0) * 8);
     r.fmt = ld_fmt;
     r.kscale = __builtin_amdgcn_raw_buffer_load_b16(ksr, ks_off + srow, 0, 0);
 #pragma unroll

@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256, 1) void qkv_quant_kernel(const QkvParams p) {
       const int64_t tt = valid ? t : wtok0;
       uint8_t* row = store + p.seg.offset[seg] +
                      ((int64_t)h * seg_len + (tt - p.seg.begin[seg])) * row_bytes;
-      uint16_t* srow = scl + ((int64_t)h * p.n_tokens + tt) * 4;
+      uint16_t* srow = scl + ((int64_t)h * p.kv_n + (tt - p.kv_row0)) * 4;
       if (fmt == FMT_INT4)
         quant_pack_store<FMT_INT4>(u, row, srow, valid);
       else

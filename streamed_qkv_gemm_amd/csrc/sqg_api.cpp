@@ -109,6 +109,80 @@ int build_layout(int64_t n, int32_t d, int32_t heads, const sqg_range* ranges, i
   return SQG_OK;
 }
 
+// Block store of keys [k0, k1): the policy's segments clipped to the block, packed one
+// after another as in a full store of k1 - k0 tokens.
+int build_block_layout(const sqg_layout& full, int32_t d, int64_t k0, int64_t k1, sqg_layout* B) {
+  if (k0 < 0 || k1 <= k0 || k1 > full.n_tokens)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "key block [%lld, %lld) is empty or outside [0, %lld]",
+                (long long)k0, (long long)k1, (long long)full.n_tokens);
+  if (k0 % 128 != 0) return fail(SQG_ERR_INVALID_ARGUMENT, "key block start %lld is not a multiple of 128",
+                                 (long long)k0);
+  std::memset(B, 0, sizeof *B);
+  B->n_tokens = k1 - k0;
+  B->n_heads = full.n_heads;
+  int64_t off = 0;
+  for (int s = 0; s < full.n_segments; ++s) {
+    const int64_t b = full.seg_begin[s] > k0 ? full.seg_begin[s] : k0;
+    const int64_t e = full.seg_end[s] < k1 ? full.seg_end[s] : k1;
+    if (b >= e) continue;
+    const int i = B->n_segments++;
+    B->seg_begin[i] = b;
+    B->seg_end[i] = e;
+    B->seg_fmt[i] = full.seg_fmt[s];
+    B->seg_row_bytes[i] = full.seg_row_bytes[s];
+    B->seg_offset[i] = off;
+    off += (int64_t)full.n_heads * (e - b) * full.seg_row_bytes[s];
+  }
+  B->pack_bytes = off;
+  B->scale_bytes = B->n_tokens * full.n_heads * 4 * 2;
+  B->q_bytes = B->n_tokens * (int64_t)d * 2;
+  B->bf16_qkv_bytes = 3 * B->q_bytes;
+  return SQG_OK;
+}
+
+// Blocks of a host-staged store with their layouts and host offsets.
+struct StagedBlock {
+  int64_t k0, k1;
+  int64_t pack_off, scale_off;  // byte offsets in the host buffers
+  sqg_layout L;
+};
+
+int staged_plan(const sqg_layout& full, int32_t d, int64_t block_rows, std::vector<StagedBlock>* out) {
+  if (block_rows <= 0 || block_rows % 128 != 0)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "block_rows must be a positive multiple of 128 (got %lld)",
+                (long long)block_rows);
+  out->clear();
+  if (full.n_tokens == 0) return SQG_OK;
+  int64_t po = 0, so = 0;
+  for (const auto& c : chunk_plan(full.n_tokens, block_rows, 512)) {
+    StagedBlock b;
+    b.k0 = c.first;
+    b.k1 = c.second;
+    b.pack_off = po;
+    b.scale_off = so;
+    const int st = build_block_layout(full, d, b.k0, b.k1, &b.L);
+    if (st != SQG_OK) return st;
+    po += b.L.pack_bytes;
+    so += b.L.scale_bytes;
+    out->push_back(b);
+  }
+  return SQG_OK;
+}
+
+int check_staged(const sqg_staged_kv* s) {
+  if (!s) return fail(SQG_ERR_INVALID_ARGUMENT, "staged is NULL");
+  if (!s->host_kpack || !s->host_vpack || !s->host_kscale || !s->host_vscale)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "a host buffer of the staged store is NULL");
+  for (int i = 0; i < 2; ++i) {
+    const void* d[] = {s->dev_kpack[i], s->dev_vpack[i], s->dev_kscale[i], s->dev_vscale[i]};
+    for (const void* ptr : d) {
+      if (!ptr) return fail(SQG_ERR_INVALID_ARGUMENT, "a device staging buffer is NULL");
+      if (!aligned16(ptr)) return fail(SQG_ERR_MISALIGNED, "staging buffer %p is not 16-byte aligned", ptr);
+    }
+  }
+  return SQG_OK;
+}
+
 sqg::SegTable seg_table(const sqg_layout& L) {
   sqg::SegTable t;
   std::memset(&t, 0, sizeof t);
@@ -188,6 +262,8 @@ int attn_prepare(const sqg_attn_args* a, bool check_q, sqg::AttnParams* p, int64
   p->q_begin = a->q_begin;
   p->q_end = q_end;
   p->q_row0 = 0;
+  p->kv_row0 = 0;
+  p->kv_n = N;
   p->d_model = a->d_model;
   p->n_heads = a->n_heads;
   p->o_dtype = a->o_dtype;
@@ -195,6 +271,85 @@ int attn_prepare(const sqg_attn_args* a, bool check_q, sqg::AttnParams* p, int64
   p->scale_log2 = (float)(scale * 1.4426950408889634);
   p->seg = seg_table(L);
   *kv_end_out = kv_end;
+  return SQG_OK;
+}
+
+// Checks the QKV-quant arguments and fills the kernel parameters (all rows, the whole
+// store).  With check_store false the K/V store pointers are not checked (the caller
+// substitutes its own).  *empty is set when there is nothing to compute.
+int qkv_prepare(const sqg_qkv_args* a, bool check_store, sqg::QkvParams* pp, sqg_layout* Lout,
+                bool* empty) {
+  *empty = false;
+  sqg_layout& L = *Lout;
+  int st = build_layout(a->n_tokens, a->d_model, a->n_heads, a->ranges, a->n_ranges, &L);
+  if (st != SQG_OK) return st;
+  const int64_t N = a->n_tokens;
+  const int64_t d = a->d_model;
+  if (d % 256 != 0)
+    return fail(SQG_ERR_UNSUPPORTED, "d_model must be a multiple of 256 (got %lld)", (long long)d);
+  if (d * a->ldw * 2 > 0x7fffffffLL || 256 * a->ldx * 2 > 0x7fffffffLL)
+    return fail(SQG_ERR_UNSUPPORTED, "W (or a 256-row slice of x) exceeds the 2 GiB a buffer resource addresses");
+  if (a->emit != SQG_EMIT_QKV && a->emit != SQG_EMIT_Q && a->emit != SQG_EMIT_KV)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "unknown emit mode %d", a->emit);
+  const bool want_q = a->emit != SQG_EMIT_KV;
+  const bool want_kv = a->emit != SQG_EMIT_Q && check_store;
+  if ((a->q_norm_w == nullptr) != (a->k_norm_w == nullptr))
+    return fail(SQG_ERR_INVALID_ARGUMENT, "q_norm_w and k_norm_w must both be set or both be NULL");
+  if ((a->rope_cos == nullptr) != (a->rope_sin == nullptr))
+    return fail(SQG_ERR_INVALID_ARGUMENT, "rope_cos and rope_sin must both be set or both be NULL");
+  if (a->q_norm_w && !(a->eps >= 0.0f && std::isfinite(a->eps)))
+    return fail(SQG_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if (a->chunk_rows < 0 || a->chunk_rows % 128 != 0)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "chunk_rows must be 0 or a positive multiple of 128 (got %lld)",
+                (long long)a->chunk_rows);
+  if (N == 0) {
+    *empty = true;
+    return SQG_OK;
+  }
+  if (!a->x || !a->w_qkv || (want_q && !a->q) ||
+      (want_kv && (!a->kpack || !a->vpack || !a->kscale || !a->vscale)))
+    return fail(SQG_ERR_INVALID_ARGUMENT, "a required device pointer is NULL");
+  const int64_t ldq = want_q ? a->ldq : d;
+  if (a->ldx < d || a->ldw < 3 * d || ldq < d)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "row strides must be >= the row length (ldx %lld, ldw %lld, ldq %lld)",
+                (long long)a->ldx, (long long)a->ldw, (long long)ldq);
+  if (a->ldx % 8 || a->ldw % 8 || ldq % 8)
+    return fail(SQG_ERR_MISALIGNED, "row strides must be multiples of 8 elements");
+  const void* ptrs[] = {a->x, a->w_qkv, want_q ? a->q : nullptr,
+                        want_kv ? a->kpack : nullptr, want_kv ? a->vpack : nullptr,
+                        want_kv ? a->kscale : nullptr, want_kv ? a->vscale : nullptr,
+                        a->q_norm_w, a->k_norm_w, a->rope_cos, a->rope_sin};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(SQG_ERR_MISALIGNED, "device pointer %p is not 16-byte aligned", p);
+
+  sqg::QkvParams& p = *pp;
+  std::memset(&p, 0, sizeof p);
+  p.x = static_cast<const uint16_t*>(a->x);
+  p.w = static_cast<const uint16_t*>(a->w_qkv);
+  p.q = want_q ? static_cast<uint16_t*>(a->q) : nullptr;
+  p.kpack = want_kv ? static_cast<uint8_t*>(a->kpack) : nullptr;
+  p.vpack = want_kv ? static_cast<uint8_t*>(a->vpack) : nullptr;
+  p.kscale = want_kv ? static_cast<uint16_t*>(a->kscale) : nullptr;
+  p.vscale = want_kv ? static_cast<uint16_t*>(a->vscale) : nullptr;
+  p.q_norm_w = a->q_norm_w;
+  p.k_norm_w = a->k_norm_w;
+  p.rope_cos = a->rope_cos;
+  p.rope_sin = a->rope_sin;
+  p.ldx = a->ldx;
+  p.ldw = a->ldw;
+  p.ldq = ldq;
+  p.n_tokens = N;
+  p.q_row0 = 0;
+  p.d_model = a->d_model;
+  p.n_heads = a->n_heads;
+  p.eps = a->eps;
+  p.col_tile0 = want_q ? 0 : (int32_t)(d / 256);
+  p.n_col_tiles = (int32_t)((want_q ? d / 256 : 0) + (a->emit != SQG_EMIT_Q ? 2 * d / 256 : 0));
+  p.seg = seg_table(L);
+  p.kv_row0 = 0;
+  p.kv_n = N;
+  p.row_begin = 0;
+  p.row_end = N;
   return SQG_OK;
 }
 
@@ -246,6 +401,7 @@ SQG_API int64_t sqg_struct_size(int which) {
     case 2: return (int64_t)sizeof(sqg_qkv_args);
     case 3: return (int64_t)sizeof(sqg_attn_args);
     case 4: return (int64_t)sizeof(sqg_qrecompute_args);
+    case 5: return (int64_t)sizeof(sqg_staged_kv);
     default: return -1;
   }
 }
@@ -271,6 +427,40 @@ SQG_API int sqg_kv_layout(int64_t n_tokens, int32_t d_model, int32_t n_heads,
   return st == SQG_OK ? ok() : st;
 }
 
+SQG_API int sqg_kv_block_layout(int64_t n_tokens, int32_t d_model, int32_t n_heads,
+                                const sqg_range* ranges, int32_t n_ranges, int64_t key_begin,
+                                int64_t key_end, sqg_layout* out) {
+  if (!out) return fail(SQG_ERR_INVALID_ARGUMENT, "out is NULL");
+  sqg_layout L;
+  int st = build_layout(n_tokens, d_model, n_heads, ranges, n_ranges, &L);
+  if (st != SQG_OK) return st;
+  st = build_block_layout(L, d_model, key_begin, key_end, out);
+  return st == SQG_OK ? ok() : st;
+}
+
+SQG_API int sqg_staged_sizes(int64_t n_tokens, int32_t d_model, int32_t n_heads,
+                             const sqg_range* ranges, int32_t n_ranges, int64_t block_rows,
+                             int64_t sizes[4], int32_t* n_blocks) {
+  if (!sizes || !n_blocks) return fail(SQG_ERR_INVALID_ARGUMENT, "sizes or n_blocks is NULL");
+  sqg_layout L;
+  int st = build_layout(n_tokens, d_model, n_heads, ranges, n_ranges, &L);
+  if (st != SQG_OK) return st;
+  std::vector<StagedBlock> blocks;
+  st = staged_plan(L, d_model, block_rows, &blocks);
+  if (st != SQG_OK) return st;
+  int64_t mp = 0, ms = 0;
+  for (const auto& b : blocks) {
+    mp = b.L.pack_bytes > mp ? b.L.pack_bytes : mp;
+    ms = b.L.scale_bytes > ms ? b.L.scale_bytes : ms;
+  }
+  sizes[0] = L.pack_bytes;
+  sizes[1] = L.scale_bytes;
+  sizes[2] = mp;
+  sizes[3] = ms;
+  *n_blocks = (int32_t)blocks.size();
+  return ok();
+}
+
 SQG_API int sqg_rope_table(int64_t pos0, int64_t n, double theta, float* cos_out, float* sin_out) {
   if (n < 0 || pos0 < 0) return fail(SQG_ERR_INVALID_ARGUMENT, "n and pos0 must be >= 0");
   if (n > 0 && (!cos_out || !sin_out)) return fail(SQG_ERR_INVALID_ARGUMENT, "output is NULL");
@@ -290,71 +480,14 @@ SQG_API int sqg_rope_table(int64_t pos0, int64_t n, double theta, float* cos_out
 
 SQG_API int sqg_streamed_qkv_quant(const sqg_qkv_args* a, void* stream) {
   if (!a) return fail(SQG_ERR_INVALID_ARGUMENT, "args is NULL");
-  sqg_layout L;
-  int st = build_layout(a->n_tokens, a->d_model, a->n_heads, a->ranges, a->n_ranges, &L);
-  if (st != SQG_OK) return st;
-  const int64_t N = a->n_tokens;
-  const int64_t d = a->d_model;
-  if (d % 256 != 0)
-    return fail(SQG_ERR_UNSUPPORTED, "d_model must be a multiple of 256 (got %lld)", (long long)d);
-  if (d * a->ldw * 2 > 0x7fffffffLL || 256 * a->ldx * 2 > 0x7fffffffLL)
-    return fail(SQG_ERR_UNSUPPORTED, "W (or a 256-row slice of x) exceeds the 2 GiB a buffer resource addresses");
-  if (a->emit != SQG_EMIT_QKV && a->emit != SQG_EMIT_Q && a->emit != SQG_EMIT_KV)
-    return fail(SQG_ERR_INVALID_ARGUMENT, "unknown emit mode %d", a->emit);
-  const bool want_q = a->emit != SQG_EMIT_KV;
-  const bool want_kv = a->emit != SQG_EMIT_Q;
-  if ((a->q_norm_w == nullptr) != (a->k_norm_w == nullptr))
-    return fail(SQG_ERR_INVALID_ARGUMENT, "q_norm_w and k_norm_w must both be set or both be NULL");
-  if ((a->rope_cos == nullptr) != (a->rope_sin == nullptr))
-    return fail(SQG_ERR_INVALID_ARGUMENT, "rope_cos and rope_sin must both be set or both be NULL");
-  if (a->q_norm_w && !(a->eps >= 0.0f && std::isfinite(a->eps)))
-    return fail(SQG_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
-  if (a->chunk_rows < 0 || a->chunk_rows % 128 != 0)
-    return fail(SQG_ERR_INVALID_ARGUMENT, "chunk_rows must be 0 or a positive multiple of 128 (got %lld)",
-                (long long)a->chunk_rows);
-  if (N == 0) return ok();
-  if (!a->x || !a->w_qkv || (want_q && !a->q) ||
-      (want_kv && (!a->kpack || !a->vpack || !a->kscale || !a->vscale)))
-    return fail(SQG_ERR_INVALID_ARGUMENT, "a required device pointer is NULL");
-  const int64_t ldq = want_q ? a->ldq : d;
-  if (a->ldx < d || a->ldw < 3 * d || ldq < d)
-    return fail(SQG_ERR_INVALID_ARGUMENT, "row strides must be >= the row length (ldx %lld, ldw %lld, ldq %lld)",
-                (long long)a->ldx, (long long)a->ldw, (long long)ldq);
-  if (a->ldx % 8 || a->ldw % 8 || ldq % 8)
-    return fail(SQG_ERR_MISALIGNED, "row strides must be multiples of 8 elements");
-  const void* ptrs[] = {a->x, a->w_qkv, want_q ? a->q : nullptr,
-                        want_kv ? a->kpack : nullptr, want_kv ? a->vpack : nullptr,
-                        want_kv ? a->kscale : nullptr, want_kv ? a->vscale : nullptr,
-                        a->q_norm_w, a->k_norm_w, a->rope_cos, a->rope_sin};
-  for (const void* p : ptrs)
-    if (p && !aligned16(p)) return fail(SQG_ERR_MISALIGNED, "device pointer %p is not 16-byte aligned", p);
-
   sqg::QkvParams p;
-  std::memset(&p, 0, sizeof p);
-  p.x = static_cast<const uint16_t*>(a->x);
-  p.w = static_cast<const uint16_t*>(a->w_qkv);
-  p.q = want_q ? static_cast<uint16_t*>(a->q) : nullptr;
-  p.kpack = want_kv ? static_cast<uint8_t*>(a->kpack) : nullptr;
-  p.vpack = want_kv ? static_cast<uint8_t*>(a->vpack) : nullptr;
-  p.kscale = want_kv ? static_cast<uint16_t*>(a->kscale) : nullptr;
-  p.vscale = want_kv ? static_cast<uint16_t*>(a->vscale) : nullptr;
-  p.q_norm_w = a->q_norm_w;
-  p.k_norm_w = a->k_norm_w;
-  p.rope_cos = a->rope_cos;
-  p.rope_sin = a->rope_sin;
-  p.ldx = a->ldx;
-  p.ldw = a->ldw;
-  p.ldq = ldq;
-  p.n_tokens = N;
-  p.q_row0 = 0;
-  p.d_model = a->d_model;
-  p.n_heads = a->n_heads;
-  p.eps = a->eps;
-  p.col_tile0 = want_q ? 0 : (int32_t)(d / 256);
-  p.n_col_tiles = (int32_t)((want_q ? d / 256 : 0) + (want_kv ? 2 * d / 256 : 0));
-  p.seg = seg_table(L);
+  sqg_layout L;
+  bool empty = false;
+  int st = qkv_prepare(a, true, &p, &L, &empty);
+  if (st != SQG_OK) return st;
+  if (empty) return ok();
   const int64_t min_tail = a->min_tail < 0 ? 512 : a->min_tail;
-  for (const auto& c : chunk_plan(N, a->chunk_rows, min_tail)) {
+  for (const auto& c : chunk_plan(a->n_tokens, a->chunk_rows, min_tail)) {
     p.row_begin = c.first;
     p.row_end = c.second;
     st = launch_status(sqg::launch_qkv_quant(p, stream), "streamed_qkv_quant launch");
@@ -437,6 +570,8 @@ SQG_API int sqg_packed_kv_attention_qrecompute(const sqg_qrecompute_args* a, voi
   qp.ldw = a->ldw;
   qp.ldq = d;
   qp.n_tokens = at.n_tokens;
+  qp.kv_row0 = 0;
+  qp.kv_n = at.n_tokens;
   qp.d_model = at.d_model;
   qp.n_heads = at.n_heads;
   qp.eps = a->eps;
@@ -460,6 +595,115 @@ SQG_API int sqg_packed_kv_attention_qrecompute(const sqg_qrecompute_args* a, voi
     cp.q_end = c1;
     cp.q_row0 = c0;
     st = attn_launch_blocks(cp, at.kv_begin, kv_end, at.kv_block, at.accumulate, stream);
+    if (st != SQG_OK) return st;
+  }
+  return ok();
+}
+
+SQG_API int sqg_streamed_qkv_quant_staged(const sqg_qkv_args* a, const sqg_staged_kv* sk,
+                                          void* stream) {
+  if (!a) return fail(SQG_ERR_INVALID_ARGUMENT, "args is NULL");
+  if (a->emit == SQG_EMIT_Q)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "emit SQG_EMIT_Q writes no K/V to stage");
+  sqg::QkvParams p;
+  sqg_layout L;
+  bool empty = false;
+  int st = qkv_prepare(a, false, &p, &L, &empty);
+  if (st != SQG_OK) return st;
+  st = check_staged(sk);
+  if (st != SQG_OK) return st;
+  std::vector<StagedBlock> blocks;
+  st = staged_plan(L, a->d_model, sk->block_rows, &blocks);
+  if (st != SQG_OK) return st;
+  if (empty) return ok();
+  for (size_t i = 0; i < blocks.size(); ++i) {
+    const StagedBlock& b = blocks[i];
+    const int j = (int)(i & 1);
+    p.kpack = static_cast<uint8_t*>(sk->dev_kpack[j]);
+    p.vpack = static_cast<uint8_t*>(sk->dev_vpack[j]);
+    p.kscale = static_cast<uint16_t*>(sk->dev_kscale[j]);
+    p.vscale = static_cast<uint16_t*>(sk->dev_vscale[j]);
+    p.seg = seg_table(b.L);
+    p.kv_row0 = b.k0;
+    p.kv_n = b.k1 - b.k0;
+    p.row_begin = b.k0;
+    p.row_end = b.k1;
+    st = launch_status(sqg::launch_qkv_quant(p, stream), "streamed_qkv_quant launch");
+    if (st != SQG_OK) return st;
+    char* hk = static_cast<char*>(sk->host_kpack) + b.pack_off;
+    char* hv = static_cast<char*>(sk->host_vpack) + b.pack_off;
+    char* hks = static_cast<char*>(sk->host_kscale) + b.scale_off;
+    char* hvs = static_cast<char*>(sk->host_vscale) + b.scale_off;
+    const int rc[4] = {
+        sqg::copy_async(hk, sk->dev_kpack[j], b.L.pack_bytes, sqg::kDeviceToHost, stream),
+        sqg::copy_async(hv, sk->dev_vpack[j], b.L.pack_bytes, sqg::kDeviceToHost, stream),
+        sqg::copy_async(hks, sk->dev_kscale[j], b.L.scale_bytes, sqg::kDeviceToHost, stream),
+        sqg::copy_async(hvs, sk->dev_vscale[j], b.L.scale_bytes, sqg::kDeviceToHost, stream)};
+    for (int r : rc) {
+      st = launch_status(r, "staging copy to host");
+      if (st != SQG_OK) return st;
+    }
+  }
+  return ok();
+}
+
+SQG_API int sqg_packed_kv_attention_staged(const sqg_attn_args* a, const sqg_staged_kv* sk,
+                                           void* stream) {
+  if (!a) return fail(SQG_ERR_INVALID_ARGUMENT, "args is NULL");
+  int st = check_staged(sk);
+  if (st != SQG_OK) return st;
+  // the store pointers are ignored: check the rest with the staging buffers in their place
+  sqg_attn_args c = *a;
+  c.kpack = sk->dev_kpack[0];
+  c.vpack = sk->dev_vpack[0];
+  c.kscale = sk->dev_kscale[0];
+  c.vscale = sk->dev_vscale[0];
+  c.kv_block = 0;
+  sqg::AttnParams p;
+  int64_t kv_end = 0;
+  bool empty = false;
+  st = attn_prepare(&c, true, &p, &kv_end, &empty);
+  if (st != SQG_OK) return st;
+  sqg_layout L;
+  st = build_layout(a->n_tokens, a->d_model, a->n_heads, a->ranges, a->n_ranges, &L);
+  if (st != SQG_OK) return st;
+  std::vector<StagedBlock> blocks;
+  st = staged_plan(L, a->d_model, sk->block_rows, &blocks);
+  if (st != SQG_OK) return st;
+  if (empty) return ok();
+  std::vector<const StagedBlock*> meet;
+  for (const auto& b : blocks)
+    if (b.k1 > a->kv_begin && b.k0 < kv_end) meet.push_back(&b);
+  if (meet.size() > 1 && (!a->lse || a->o_dtype != SQG_F32))
+    return fail(SQG_ERR_INVALID_ARGUMENT, "the key range spans %d blocks: merging needs an lse buffer and o_dtype SQG_F32",
+                (int)meet.size());
+  for (size_t i = 0; i < meet.size(); ++i) {
+    const StagedBlock& b = *meet[i];
+    const int j = (int)(i & 1);
+    const char* hk = static_cast<const char*>(sk->host_kpack) + b.pack_off;
+    const char* hv = static_cast<const char*>(sk->host_vpack) + b.pack_off;
+    const char* hks = static_cast<const char*>(sk->host_kscale) + b.scale_off;
+    const char* hvs = static_cast<const char*>(sk->host_vscale) + b.scale_off;
+    const int rc[4] = {
+        sqg::copy_async(sk->dev_kpack[j], hk, b.L.pack_bytes, sqg::kHostToDevice, stream),
+        sqg::copy_async(sk->dev_vpack[j], hv, b.L.pack_bytes, sqg::kHostToDevice, stream),
+        sqg::copy_async(sk->dev_kscale[j], hks, b.L.scale_bytes, sqg::kHostToDevice, stream),
+        sqg::copy_async(sk->dev_vscale[j], hvs, b.L.scale_bytes, sqg::kHostToDevice, stream)};
+    for (int r : rc) {
+      st = launch_status(r, "staging copy to device");
+      if (st != SQG_OK) return st;
+    }
+    p.kpack = static_cast<const uint8_t*>(sk->dev_kpack[j]);
+    p.vpack = static_cast<const uint8_t*>(sk->dev_vpack[j]);
+    p.kscale = static_cast<const uint16_t*>(sk->dev_kscale[j]);
+    p.vscale = static_cast<const uint16_t*>(sk->dev_vscale[j]);
+    p.seg = seg_table(b.L);
+    p.kv_row0 = b.k0;
+    p.kv_n = b.k1 - b.k0;
+    p.kv_begin = b.k0 > a->kv_begin ? b.k0 : a->kv_begin;
+    p.kv_end = b.k1 < kv_end ? b.k1 : kv_end;
+    p.accumulate = i == 0 ? a->accumulate : 1;
+    st = launch_status(sqg::launch_packed_attention(p, stream), "packed_kv_attention launch");
     if (st != SQG_OK) return st;
   }
   return ok();

@@ -80,6 +80,4 @@ int launch_test_fwht(const float* in, float* out, int64_t rows, int32_t normaliz
   return (int)hipGetLastError();
 }
 
-const char* hip_error_text(int err) { return hipGetErrorString((hipError_t)err); }
-
 }  // namespace sqg

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 10
     for n in names:
         assert hasattr(lib, n), n
-    assert sqg.version() == 100
+    assert sqg.version() == 110
 
 
 def test_struct_sizes_match_binding():
@@ -40,6 +40,7 @@ def test_struct_sizes_match_binding():
     assert lib.sqg_struct_size(2) == ctypes.sizeof(B.QkvArgs)
     assert lib.sqg_struct_size(3) == ctypes.sizeof(B.AttnArgs)
     assert lib.sqg_struct_size(4) == ctypes.sizeof(B.QRecomputeArgs)
+    assert lib.sqg_struct_size(5) == ctypes.sizeof(B.StagedKV)
     assert lib.sqg_struct_size(9) == -1
 
 
@@ -288,3 +289,92 @@ def test_binding_refuses_cpu_tensors():
     w = torch.zeros((256, 768), dtype=torch.bfloat16)
     with pytest.raises((ValueError, RuntimeError)):
         sqg.streamed_qkv_quant(x, w, out={"q": x, "kpack": x, "vpack": x, "kscale": x, "vscale": x})
+
+
+# ----------------------------------------------------------------------------- host-staged store
+STAGE_POLICY = [(0, 384, 1), (384, 1024, 0), (1024, 2304, 1), (2304, 2900, 0)]
+
+
+@pytest.mark.parametrize("k0,k1", [(0, 2900), (0, 512), (256, 1280), (1024, 2900), (2816, 2900),
+                                   (384, 1000)])
+def test_block_layout_is_the_layout_of_the_clipped_policy(k0, k1):
+    # a block store is the store of the shorter sequence whose policy is the clipped one
+    H = 4
+    B_ = sqg.kv_block_layout(2900, 512, k0, k1, STAGE_POLICY)
+    clipped = [(max(b, k0) - k0, min(e, k1) - k0, f) for b, e, f in STAGE_POLICY if min(e, k1) > max(b, k0)]
+    want, total = oracle.packed_layout(k1 - k0, H, clipped)
+    assert B_["n_tokens"] == k1 - k0
+    assert len(B_["segments"]) == len(want)
+    for got, w in zip(B_["segments"], want):
+        assert (got["begin"] - k0, got["end"] - k0, got["fmt"], got["offset"], got["row_bytes"]) == \
+            (w["begin"], w["end"], w["fmt"], w["offset"], w["row_bytes"])
+    assert B_["scale_bytes"] == H * (k1 - k0) * 8 and B_["pack_bytes"] == total
+
+
+@pytest.mark.parametrize("k0,k1", [(100, 900), (0, 0), (512, 256), (0, 3000), (-128, 128)])
+def test_block_layout_rejects_bad_blocks(k0, k1):
+    with pytest.raises(sqg.SqgError):
+        sqg.kv_block_layout(2900, 512, k0, k1, STAGE_POLICY)
+
+
+@pytest.mark.parametrize("block,nb", [(512, 5), (1024, 3), (128, 22), (4096, 1)])
+def test_staged_sizes_sum_the_blocks(block, nb):
+    (hp, hs, dp, ds), n_blocks = sqg.staged_sizes(2900, 512, block, STAGE_POLICY)
+    full = sqg.kv_layout(2900, 512, STAGE_POLICY)
+    assert n_blocks == nb
+    assert hp == full["pack_bytes"] and hs == full["scale_bytes"]
+    plan = sqg.chunk_ranges(2900, block, 512)
+    assert len(plan) == nb
+    blocks = [sqg.kv_block_layout(2900, 512, b, e, STAGE_POLICY) for b, e in plan]
+    assert sum(b["pack_bytes"] for b in blocks) == hp
+    assert dp == max(b["pack_bytes"] for b in blocks) and ds == max(b["scale_bytes"] for b in blocks)
+
+
+def staged_struct(**kw):
+    s = B.StagedKV()
+    s.block_rows = 512
+    s.host_kpack = s.host_vpack = s.host_kscale = s.host_vscale = FAKE
+    for k in ("dev_kpack", "dev_vpack", "dev_kscale", "dev_vscale"):
+        arr = getattr(s, k)
+        arr[0], arr[1] = FAKE, FAKE + 4096
+    for k, v in kw.items():
+        if k.endswith("_1"):
+            getattr(s, k[:-2])[1] = v
+        else:
+            setattr(s, k, v)
+    return s
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(block_rows=100), -1, b"block_rows"),
+    (dict(block_rows=0), -1, b"block_rows"),
+    (dict(host_vscale=None), -1, b"host"),
+    (dict(dev_vpack_1=None), -1, b"staging"),
+    (dict(dev_kscale_1=FAKE + 8), -3, b"aligned"),
+])
+def test_staged_argument_errors(kw, status, msg):
+    lib = sqg.load()
+    s = staged_struct(**kw)
+    a = qkv_args(kpack=None, vpack=None, kscale=None, vscale=None)
+    assert lib.sqg_streamed_qkv_quant_staged(ctypes.byref(a), ctypes.byref(s), None) == status
+    assert msg in lib.sqg_last_error()
+    b = attn_args(kpack=None, vpack=None, kscale=None, vscale=None)
+    assert lib.sqg_packed_kv_attention_staged(ctypes.byref(b), ctypes.byref(s), None) == status
+    assert msg in lib.sqg_last_error()
+
+
+def test_staged_entry_specific_errors():
+    lib = sqg.load()
+    s = staged_struct()
+    assert lib.sqg_streamed_qkv_quant_staged(ctypes.byref(qkv_args(emit=1)), ctypes.byref(s), None) == -1
+    assert b"SQG_EMIT_Q" in lib.sqg_last_error()
+    assert lib.sqg_streamed_qkv_quant_staged(ctypes.byref(qkv_args()), None, None) == -1
+    # 1024 keys in 512-key blocks: two blocks need the LSE merge
+    b = attn_args(lse=None)
+    assert lib.sqg_packed_kv_attention_staged(ctypes.byref(b), ctypes.byref(s), None) == -1
+    assert b"spans 2 blocks" in lib.sqg_last_error()
+    b = attn_args(o_dtype=1)
+    assert lib.sqg_packed_kv_attention_staged(ctypes.byref(b), ctypes.byref(s), None) == -1
+    # empty query range: nothing to do
+    b = attn_args(q_begin=5, q_end=5)
+    assert lib.sqg_packed_kv_attention_staged(ctypes.byref(b), ctypes.byref(s), None) == 0
