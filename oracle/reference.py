@@ -16,7 +16,8 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
-    "HEAD_DIM", "GROUP", "INT4", "INT8", "QMAX", "ROW_BYTES", "SCALE_BITS", "round_up_bits",
+    "HEAD_DIM", "GROUP", "INT4", "INT8", "BF16", "FORMATS", "QMAX", "ROW_BYTES", "SCALE_BITS",
+    "round_up_bits", "segment_parts", "head_formats", "gather_bf16_rows",
     "hadamard_pm1", "rotation_matrix",
     "f32_to_bf16_bits", "bf16_bits_to_f64", "f32_to_f16",
     "chunk_ranges", "range_segments", "token_formats",
@@ -31,10 +32,12 @@ __all__ = [
 
 HEAD_DIM = 128          # head dimension of every workload ([VL] docstring: 7168 = 56 x 128)
 GROUP = 32              # quantisation group along head_dim (the workloads' "group 32")
-INT4 = 0                # token-range formats ([FR] "Mixed precision for conditioning")
-INT8 = 1
+INT4 = 0                # token-range formats ([FR] "Mixed precision for conditioning":
+INT8 = 1                # conditioning ranges at BF16 or INT8, generated tokens at
+BF16 = 2                # rotated INT4)
+FORMATS = (INT4, INT8, BF16)
 QMAX = {INT4: 7, INT8: 127}
-ROW_BYTES = {INT4: HEAD_DIM // 2, INT8: HEAD_DIM}
+ROW_BYTES = {INT4: HEAD_DIM // 2, INT8: HEAD_DIM, BF16: 2 * HEAD_DIM}
 # significant bits kept in a group scale: code bits + scale bits <= 11, so code * scale
 # is exact in fp16 (INT4 codes need 3 bits, INT8 codes 7)
 SCALE_BITS = {INT4: 8, INT8: 4}
@@ -94,40 +97,71 @@ def chunk_ranges(n: int, size: int, min_tail: int = 512) -> List[Tuple[int, int]
 
 
 def range_segments(n: int, ranges: Optional[Sequence[Tuple[int, int, int]]],
-                   boundary_multiple: int = 128) -> List[Tuple[int, int, int]]:
+                   boundary_multiple: int = 128,
+                   n_heads: Optional[int] = None) -> List[Tuple[int, int, int]]:
     """Validate a token-range precision policy and return its segments.
 
     [FR] "Mixed precision for conditioning": different K/V precision per token
-    range of the packed sequence (conditioning ranges at 8 bits, generated tokens
-    at rotated 4 bits).  [VL] segments are half-open (a, b) pairs in order.
+    range of the packed sequence (conditioning ranges at BF16 or 8 bits, generated
+    tokens at rotated 4 bits).  [VL] segments are half-open (a, b) pairs in order.
     Reading: the ranges must be sorted, contiguous, non-empty and cover [0, n);
     every interior boundary is a multiple of `boundary_multiple` so that key tiles
-    never straddle two formats.  No ranges means one INT4 range."""
+    never straddle two formats.  No ranges means one INT4 range.
+
+    A range may carry a fourth entry, a bit mask of heads whose K/V are kept at
+    INT8 inside an INT4 range ([VL] kvmix section: a per-head 4/8-bit split, "hi"
+    heads at 8 bits and the rest at 4).  Reading: the mask applies to INT4 ranges
+    only; segments with a non-zero mask come back as (b, e, f, mask)."""
     if not ranges:
         return [(0, n, INT4)] if n > 0 else []
     segs = []
     pos = 0
     for r in ranges:
         b, e, f = int(r[0]), int(r[1]), int(r[2])
-        if f not in (INT4, INT8):
+        m = int(r[3]) if len(r) > 3 else 0
+        if f not in FORMATS:
             raise ValueError("unknown format %r" % f)
+        if m < 0 or m >= 1 << 64:
+            raise ValueError("head mask out of range")
+        if m and f != INT4:
+            raise ValueError("a head mask applies to INT4 ranges only")
+        if n_heads is not None and m >> n_heads:
+            raise ValueError("head mask names a head >= n_heads")
         if b != pos:
             raise ValueError("ranges must be contiguous from 0 (gap or overlap at %d)" % b)
         if e <= b:
             raise ValueError("empty or reversed range")
         if e < n and e % boundary_multiple:
             raise ValueError("interior boundary %d is not a multiple of %d" % (e, boundary_multiple))
-        segs.append((b, e, f))
+        segs.append((b, e, f, m) if m else (b, e, f))
         pos = e
     if pos != n:
         raise ValueError("ranges end at %d, not at n=%d" % (pos, n))
     return segs
 
 
+def segment_parts(seg) -> Tuple[int, int, int, int]:
+    """(begin, end, format, INT8 head mask) of a segment given as 3 or 4 entries."""
+    return int(seg[0]), int(seg[1]), int(seg[2]), int(seg[3]) if len(seg) > 3 else 0
+
+
 def token_formats(n: int, segments: Sequence[Tuple[int, int, int]]) -> np.ndarray:
+    """Format of each token's range (the per-head INT8 mask aside)."""
     fm = np.empty(n, dtype=np.int64)
-    for b, e, f in segments:
+    for seg in segments:
+        b, e, f, _ = segment_parts(seg)
         fm[b:e] = f
+    return fm
+
+
+def head_formats(n: int, n_heads: int, segments) -> np.ndarray:
+    """Format of each (token, head): the range's format, or INT8 for a head whose
+    bit is set in an INT4 range's mask ([VL] kvmix)."""
+    fm = np.empty((n, n_heads), dtype=np.int64)
+    for seg in segments:
+        b, e, f, m = segment_parts(seg)
+        for h in range(n_heads):
+            fm[b:e, h] = INT8 if (f == INT4 and (m >> h) & 1) else f
     return fm
 
 
@@ -282,10 +316,15 @@ def qkv_quant_rows(x_bits_rows: np.ndarray, w_bits: np.ndarray, n_heads: int,
     projection; Q is kept in bf16; K and V are rotated, quantised and packed.
     [VL] block section, `_phase1_kv`: projection -> split -> (RMSNorm + RoPE of q
     and k) -> store.  Row r uses token position positions[r] for RoPE and format
-    fmts[r] (INT4 or INT8) for its K/V codes.
+    fmts[r] (INT4, INT8 or BF16; or fmts[r, h] per head) for its K/V.
 
     Returns q_bits [R, d] uint16 (bf16, model basis), k_codes / v_codes
-    [R, H, 128] int8, k_scales / v_scales [R, H, 4] fp16."""
+    [R, H, 128] int8, k_scales / v_scales [R, H, 4] fp16 (zero where the format
+    is BF16) and k_bf16 / v_bf16 [R, H, 128] uint16: the rotated fp32 values
+    rounded to bf16 where the format is BF16 (zero elsewhere).  Reading of [FR]
+    "Mixed precision for conditioning": a BF16 range keeps K/V at 16 bits in the
+    same rotated basis as the low-bit ranges (the rotation is orthogonal, so this
+    keeps what bf16 K/V in the model basis keep: 8 significant bits)."""
     y = project(x_bits_rows, w_bits)
     q, k, v = split_heads(y, n_heads)
     if q_norm_w is not None:
@@ -300,17 +339,25 @@ def qkv_quant_rows(x_bits_rows: np.ndarray, w_bits: np.ndarray, n_heads: int,
     kr = rotate(k)
     vr = rotate(v)
     out = {"q_bits": q_bits}
+    fm = np.asarray(fmts, dtype=np.int64)
+    if fm.ndim == 1:
+        fm = np.repeat(fm[:, None], n_heads, axis=1)
     for name, rr in (("k", kr), ("v", vr)):
         codes = np.zeros(rr.shape, dtype=np.int8)
         scales = np.zeros(rr.shape[:-1] + (HEAD_DIM // GROUP,), dtype=np.float16)
+        bf = np.zeros(rr.shape, dtype=np.uint16)
         for f in (INT4, INT8):
-            sel = np.asarray(fmts) == f
+            sel = fm == f
             if np.any(sel):
                 c, s = quantize_groups(rr[sel], QMAX[f])
                 codes[sel] = c
                 scales[sel] = s
+        sel = fm == BF16
+        if np.any(sel):
+            bf[sel] = f32_to_bf16_bits(rr[sel])
         out[name + "_codes"] = codes
         out[name + "_scales"] = scales
+        out[name + "_bf16"] = bf
     out["k_rot_f32"] = kr
     out["v_rot_f32"] = vr
     return out
@@ -322,21 +369,35 @@ def packed_layout(n: int, n_heads: int, segments: Sequence[Tuple[int, int, int]]
 
     Reading of [FR] "Proposed backend capability" / "Quality-oriented low-bit
     format" (fixed-width packed tiles a kernel can address directly) and of [VL]
-    kvi8r (head-major [heads, tokens, head_dim] store): each segment [b, e) of
-    format f holds its codes head-major, row (h, t) at
-    offset_s + (h * (e - b) + (t - b)) * row_bytes(f); segments follow each other.
-    Scales are separate, fp16 [H, N, 4] over the whole sequence."""
+    kvi8r (head-major [heads, tokens, head_dim] store): each segment [b, e) holds
+    its rows head-major, head after head; head h of the segment uses format
+    fmt(h) (the segment's, or INT8 for a masked head of an INT4 segment) and
+    starts at offset_s + (e - b) * (sum of row_bytes(fmt(h')) over h' < h); row
+    (h, t) sits at that start + (t - b) * row_bytes(fmt(h)).  Segments follow each
+    other.  Scales are separate, fp16 [H, N, 4] over the whole sequence (zero and
+    unused for BF16 rows)."""
     out = []
     off = 0
-    for b, e, f in segments:
-        out.append({"begin": b, "end": e, "fmt": f, "offset": off, "row_bytes": ROW_BYTES[f]})
-        off += n_heads * (e - b) * ROW_BYTES[f]
+    for seg in segments:
+        b, e, f, m = segment_parts(seg)
+        hf = [INT8 if (f == INT4 and (m >> h) & 1) else f for h in range(n_heads)]
+        hrb = [ROW_BYTES[x] for x in hf]
+        hoff = []
+        o = off
+        for h in range(n_heads):
+            hoff.append(o)
+            o += (e - b) * hrb[h]
+        out.append({"begin": b, "end": e, "fmt": f, "int8_heads": m, "offset": off,
+                    "row_bytes": ROW_BYTES[f], "head_fmt": hf, "head_row_bytes": hrb,
+                    "head_offset": hoff})
+        off = o
     return out, off
 
 
 def gather_packed_rows(packed: np.ndarray, scales: np.ndarray, layout, n_heads: int,
                        rows: np.ndarray):
-    """Codes [R, H, 128] int8 and scales [R, H, 4] fp16 of the given token rows."""
+    """Codes [R, H, 128] int8 and scales [R, H, 4] fp16 of the given token rows
+    (codes stay zero for BF16 rows: see gather_bf16_rows)."""
     packed = np.asarray(packed, dtype=np.uint8).reshape(-1)
     sc = np.asarray(scales).reshape(n_heads, -1, HEAD_DIM // GROUP)
     rows = np.asarray(rows, dtype=np.int64)
@@ -345,13 +406,33 @@ def gather_packed_rows(packed: np.ndarray, scales: np.ndarray, layout, n_heads: 
         sel = np.nonzero((rows >= seg["begin"]) & (rows < seg["end"]))[0]
         if sel.size == 0:
             continue
-        rb = seg["row_bytes"]
-        L = seg["end"] - seg["begin"]
         for h in range(n_heads):
-            start = seg["offset"] + (h * L + (rows[sel] - seg["begin"])) * rb
+            f, rb = seg["head_fmt"][h], seg["head_row_bytes"][h]
+            if f == BF16:
+                continue
+            start = seg["head_offset"][h] + (rows[sel] - seg["begin"]) * rb
             idx = start[:, None] + np.arange(rb)[None, :]
-            codes[sel, h] = unpack_codes(packed[idx], seg["fmt"])
+            codes[sel, h] = unpack_codes(packed[idx], f)
     return codes, np.ascontiguousarray(sc[:, rows, :].transpose(1, 0, 2))
+
+
+def gather_bf16_rows(packed: np.ndarray, layout, n_heads: int, rows: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns [R, H, 128] uint16 of the given rows where the format is
+    BF16 (zero elsewhere); each row is 128 little-endian bf16 values."""
+    packed = np.asarray(packed, dtype=np.uint8).reshape(-1)
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.zeros((rows.size, n_heads, HEAD_DIM), dtype=np.uint16)
+    for seg in layout:
+        sel = np.nonzero((rows >= seg["begin"]) & (rows < seg["end"]))[0]
+        if sel.size == 0:
+            continue
+        for h in range(n_heads):
+            if seg["head_fmt"][h] != BF16:
+                continue
+            start = seg["head_offset"][h] + (rows[sel] - seg["begin"]) * ROW_BYTES[BF16]
+            idx = start[:, None] + np.arange(ROW_BYTES[BF16])[None, :]
+            out[sel, h] = np.ascontiguousarray(packed[idx]).view(np.uint16)
+    return out
 
 
 def decode_head(packed: np.ndarray, scales: np.ndarray, layout, n_heads: int, head: int,
@@ -364,11 +445,13 @@ def decode_head(packed: np.ndarray, scales: np.ndarray, layout, n_heads: int, he
         lo, hi = max(begin, seg["begin"]), min(end, seg["end"])
         if lo >= hi:
             continue
-        rb = seg["row_bytes"]
-        L = seg["end"] - seg["begin"]
-        start = seg["offset"] + (head * L + (lo - seg["begin"])) * rb
-        blob = packed[start:start + (hi - lo) * rb].reshape(hi - lo, rb)
-        out[lo - begin:hi - begin] = dequantize(unpack_codes(blob, seg["fmt"]), sc[head, lo:hi])
+        f, rb = seg["head_fmt"][head], seg["head_row_bytes"][head]
+        start = seg["head_offset"][head] + (lo - seg["begin"]) * rb
+        blob = np.ascontiguousarray(packed[start:start + (hi - lo) * rb].reshape(hi - lo, rb))
+        if f == BF16:
+            out[lo - begin:hi - begin] = bf16_bits_to_f64(blob.view(np.uint16))
+        else:
+            out[lo - begin:hi - begin] = dequantize(unpack_codes(blob, f), sc[head, lo:hi])
     return out
 
 
@@ -471,7 +554,7 @@ def working_set_bytes(n: int, d_model: int, segments: Sequence[Tuple[int, int, i
     """Closed-form bytes of the fused bf16 QKV versus Q bf16 + packed K/V + scales.
     [FR] "Potential reduction": Q kept at bf16, K and V at 4 bits, plus metadata."""
     H = d_model // HEAD_DIM
-    codes = sum((e - b) * H * ROW_BYTES[f] for b, e, f in segments)
+    _, codes = packed_layout(n, H, segments)
     scales = n * H * (HEAD_DIM // GROUP) * 2
     q = 2 * n * d_model
     return {"bf16_qkv": 6 * n * d_model, "q": q, "k_codes": codes, "v_codes": codes,
