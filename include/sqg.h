@@ -36,7 +36,7 @@ extern "C" {
 #define SQG_API
 #endif
 
-#define SQG_VERSION 110          /* 1.1.0 */
+#define SQG_VERSION 120          /* 1.2.0 */
 #define SQG_HEAD_DIM 128
 #define SQG_GROUP 32
 #define SQG_MAX_SEGMENTS 16
@@ -51,11 +51,16 @@ typedef enum sqg_status {
 
 /* K/V storage format of a token range.  [FR] "Quality-oriented low-bit format"
  * (fixed-width rotated INT4 with per-group scales) and "Mixed precision for
- * conditioning" (8-bit K/V for conditioning ranges).  Both formats hold codes of
- * the Hadamard-rotated vector with one fp16 scale per group of 32 values. */
+ * conditioning" (BF16 or 8-bit K/V for conditioning ranges).  The integer formats
+ * hold codes of the Hadamard-rotated vector with one fp16 scale per group of 32
+ * values; BF16 holds the rotated vector itself. */
 typedef enum sqg_kv_format {
   SQG_INT4_ROT = 0,   /* codes in [-7, 7], two per byte, code 2i in bits 0-3 */
-  SQG_INT8_ROT = 1    /* codes in [-127, 127], one per byte (two's complement) */
+  SQG_INT8_ROT = 1,   /* codes in [-127, 127], one per byte (two's complement) */
+  SQG_BF16_ROT = 2    /* the rotated values rounded to bf16 (RNE), 128 per row, little
+                         endian; no scales (their entries are written as zero).  [FR]
+                         "Mixed precision for conditioning" keeps conditioning ranges
+                         at BF16 or INT8. */
 } sqg_kv_format;
 
 typedef enum sqg_out_dtype { SQG_F32 = 0, SQG_BF16 = 1, SQG_F16 = 2 } sqg_out_dtype;
@@ -74,15 +79,23 @@ typedef enum sqg_emit {
 typedef struct sqg_range {
   int64_t begin;
   int64_t end;
-  int32_t fmt;        /* sqg_kv_format */
-  int32_t reserved;   /* must be 0 */
+  int32_t fmt;          /* sqg_kv_format */
+  int32_t reserved;     /* must be 0 */
+  uint64_t int8_heads;  /* INT4 ranges only (else 0): bit h set = head h of this range
+                           is stored SQG_INT8_ROT ([VL] kvmix section: per-head 4/8-bit
+                           split); bits at or above n_heads must be 0 */
 } sqg_range;
 
 /* Byte layout of the packed K (and, identically, V) store, filled by sqg_kv_layout.
- * Segment s covers tokens [seg_begin[s], seg_end[s]) in format seg_fmt[s]; the
- * codes of (head h, token t) start at byte
- *   seg_offset[s] + (h * (seg_end[s] - seg_begin[s]) + (t - seg_begin[s])) * seg_row_bytes[s]
- * of the kpack (vpack) buffer, where seg_row_bytes is 64 for INT4 and 128 for INT8.
+ * Segment s covers tokens [seg_begin[s], seg_end[s]) in format seg_fmt[s], except that
+ * in an INT4 segment the heads set in seg_int8_heads[s] are INT8.  Row bytes are 64
+ * (INT4), 128 (INT8) and 256 (BF16); seg_row_bytes[s] is that of seg_fmt[s].  Within
+ * a segment the heads' rows follow each other, head by head: the row of (head h,
+ * token t) starts at byte
+ *   seg_offset[s] + L * (sum of the row bytes of heads 0 .. h-1) + (t - seg_begin[s]) * rb(h)
+ * of the kpack (vpack) buffer, L = seg_end[s] - seg_begin[s]; sqg_kv_row_offset
+ * computes it.  With no INT8 heads this is
+ *   seg_offset[s] + (h * L + (t - seg_begin[s])) * seg_row_bytes[s].
  * Scales are fp16 [n_heads, n_tokens, 4]: group g of (h, t) at element (h*N + t)*4 + g.
  * A block store (sqg_kv_block_layout) holds only keys [k0, k1): n_tokens = k1 - k0, the
  * segments are the policy's clipped to [k0, k1) (seg_begin/seg_end stay absolute token
@@ -96,6 +109,7 @@ typedef struct sqg_layout {
   int64_t seg_offset[SQG_MAX_SEGMENTS];
   int32_t seg_fmt[SQG_MAX_SEGMENTS];
   int32_t seg_row_bytes[SQG_MAX_SEGMENTS];
+  uint64_t seg_int8_heads[SQG_MAX_SEGMENTS];
   int64_t q_bytes;        /* bf16 Q [N, d] */
   int64_t pack_bytes;     /* bytes of kpack, and of vpack */
   int64_t scale_bytes;    /* bytes of kscale, and of vscale */
@@ -221,9 +235,14 @@ SQG_API int sqg_chunk_ranges(int64_t n, int64_t size, int64_t min_tail, int64_t*
  * conditioning") and fills the packed-store layout.  Ranges must be sorted,
  * contiguous, non-empty, cover [0, n_tokens), have interior boundaries that are
  * multiples of 128, and number at most SQG_MAX_SEGMENTS; n_ranges 0 = all INT4.
- * d_model must be 128 * n_heads. */
+ * d_model must be 128 * n_heads, n_heads at most 64. */
 SQG_API int sqg_kv_layout(int64_t n_tokens, int32_t d_model, int32_t n_heads,
                           const sqg_range* ranges, int32_t n_ranges, sqg_layout* out);
+
+/* Host only.  Byte offset of the row of (head, token) in the kpack (vpack) buffer
+ * laid out by *layout (a full or a block store); -1 if the head or the token is
+ * outside the layout. */
+SQG_API int64_t sqg_kv_row_offset(const sqg_layout* layout, int32_t head, int64_t token);
 
 /* Host only.  Layout of the block store that holds keys [key_begin, key_end) of the
  * sequence the policy describes (see sqg_layout).  key_begin must be a multiple of 128

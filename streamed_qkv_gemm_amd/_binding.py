@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(PKG, "libsqg.so")
 
 SQG_INT4_ROT = 0
 SQG_INT8_ROT = 1
+SQG_BF16_ROT = 2
 SQG_F32, SQG_BF16, SQG_F16 = 0, 1, 2
 SQG_EMIT_QKV, SQG_EMIT_Q, SQG_EMIT_KV = 0, 1, 2
 MAX_SEGMENTS = 16
@@ -35,14 +36,16 @@ class SqgError(RuntimeError):
 
 
 class Range(ctypes.Structure):
-    _fields_ = [("begin", _c_i64), ("end", _c_i64), ("fmt", _c_i32), ("reserved", _c_i32)]
+    _fields_ = [("begin", _c_i64), ("end", _c_i64), ("fmt", _c_i32), ("reserved", _c_i32),
+                ("int8_heads", ctypes.c_uint64)]
 
 
 class Layout(ctypes.Structure):
     _fields_ = [("n_tokens", _c_i64), ("n_heads", _c_i32), ("n_segments", _c_i32),
                 ("seg_begin", _c_i64 * MAX_SEGMENTS), ("seg_end", _c_i64 * MAX_SEGMENTS),
                 ("seg_offset", _c_i64 * MAX_SEGMENTS), ("seg_fmt", _c_i32 * MAX_SEGMENTS),
-                ("seg_row_bytes", _c_i32 * MAX_SEGMENTS), ("q_bytes", _c_i64),
+                ("seg_row_bytes", _c_i32 * MAX_SEGMENTS),
+                ("seg_int8_heads", ctypes.c_uint64 * MAX_SEGMENTS), ("q_bytes", _c_i64),
                 ("pack_bytes", _c_i64), ("scale_bytes", _c_i64), ("bf16_qkv_bytes", _c_i64)]
 
 
@@ -106,6 +109,8 @@ def load(path: Optional[str] = None):
     lib.sqg_rope_table.argtypes = [_c_i64, _c_i64, ctypes.c_double, _vp, _vp]
     lib.sqg_streamed_qkv_quant.argtypes = [ctypes.POINTER(QkvArgs), _vp]
     lib.sqg_packed_kv_attention.argtypes = [ctypes.POINTER(AttnArgs), _vp]
+    lib.sqg_kv_row_offset.restype = _c_i64
+    lib.sqg_kv_row_offset.argtypes = [ctypes.POINTER(Layout), _c_i32, _c_i64]
     lib.sqg_kv_block_layout.argtypes = [_c_i64, _c_i32, _c_i32, ctypes.POINTER(Range), _c_i32,
                                         _c_i64, _c_i64, ctypes.POINTER(Layout)]
     lib.sqg_staged_sizes.argtypes = [_c_i64, _c_i32, _c_i32, ctypes.POINTER(Range), _c_i32, _c_i64,
@@ -141,8 +146,9 @@ def _ranges_array(ranges: Optional[Sequence[Tuple[int, int, int]]]):
     if not ranges:
         return None, 0
     arr = (Range * len(ranges))()
-    for i, (b, e, f) in enumerate(ranges):
-        arr[i].begin, arr[i].end, arr[i].fmt, arr[i].reserved = int(b), int(e), int(f), 0
+    for i, r in enumerate(ranges):
+        arr[i].begin, arr[i].end, arr[i].fmt, arr[i].reserved = int(r[0]), int(r[1]), int(r[2]), 0
+        arr[i].int8_heads = int(r[3]) if len(r) > 3 else 0
     return arr, len(ranges)
 
 
@@ -175,10 +181,16 @@ def chunk_ranges(n: int, size: int, min_tail: int = 512):
 
 def _layout_dict(L) -> Dict:
     segs = [{"begin": L.seg_begin[i], "end": L.seg_end[i], "fmt": L.seg_fmt[i],
-             "offset": L.seg_offset[i], "row_bytes": L.seg_row_bytes[i]} for i in range(L.n_segments)]
+             "int8_heads": L.seg_int8_heads[i], "offset": L.seg_offset[i],
+             "row_bytes": L.seg_row_bytes[i]} for i in range(L.n_segments)]
     return {"n_tokens": L.n_tokens, "n_heads": L.n_heads, "segments": segs,
             "q_bytes": L.q_bytes, "pack_bytes": L.pack_bytes, "scale_bytes": L.scale_bytes,
-            "bf16_qkv_bytes": L.bf16_qkv_bytes}
+            "bf16_qkv_bytes": L.bf16_qkv_bytes, "_struct": L}
+
+
+def kv_row_offset(layout: Dict, head: int, token: int) -> int:
+    """Byte offset of the row of (head, token) in a store laid out by `layout`."""
+    return load().sqg_kv_row_offset(ctypes.byref(layout["_struct"]), head, token)
 
 
 def kv_block_layout(n_tokens: int, d_model: int, key_begin: int, key_end: int, ranges=None) -> Dict:

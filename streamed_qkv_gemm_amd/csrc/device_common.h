@@ -194,6 +194,42 @@ __device__ __forceinline__ void quant_pack_store(const float (&r)[4][16], uint8_
   }
 }
 
+// Format, row bytes and first byte of head h's rows in segment sg (see SegTable):
+// an INT4 segment's INT8 heads take 64 bytes more per row than the others.
+__device__ __forceinline__ int head_format(const SegTable& t, int sg, int h) {
+  return (t.fmt[sg] == FMT_INT4 && ((t.int8_heads[sg] >> h) & 1ull)) ? FMT_INT8 : t.fmt[sg];
+}
+__device__ __forceinline__ int format_row_bytes(int fmt) {
+  return fmt == FMT_INT4 ? 64 : (fmt == FMT_INT8 ? 128 : 256);
+}
+__device__ __forceinline__ int64_t head_rows_offset(const SegTable& t, int sg, int h) {
+  int64_t units = (int64_t)format_row_bytes(t.fmt[sg]) * h;
+  const uint64_t below = t.int8_heads[sg] & ((1ull << h) - 1ull);
+  units += 64 * (int64_t)__popcll(below);
+  return t.offset[sg] + (t.end[sg] - t.begin[sg]) * units;
+}
+
+// One rotated 128-vector per lane pair (column layout) rounded to bf16 (RNE) and
+// stored as 128 consecutive bf16 values; the group scales of such a row are zero.
+__device__ __forceinline__ void bf16_row_store(const float (&r)[4][16], uint8_t* row,
+                                               uint16_t* scales, bool valid) {
+  const int h4 = upper_half() ? 4 : 0;
+  if (!valid) return;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      u32x2 v;
+      v[0] = f32_to_bf16_bits(r[b][4 * q]) | (f32_to_bf16_bits(r[b][4 * q + 1]) << 16);
+      v[1] = f32_to_bf16_bits(r[b][4 * q + 2]) | (f32_to_bf16_bits(r[b][4 * q + 3]) << 16);
+      *reinterpret_cast<u32x2*>(row + 2 * (32 * b + 8 * q + h4)) = v;
+    }
+  if (!upper_half()) {
+    u32x2 z = {0u, 0u};
+    *reinterpret_cast<u32x2*>(scales) = z;
+  }
+}
+
 // segment of a token (the table is small and uniform across the wave)
 __device__ __forceinline__ int find_segment(const SegTable& t, int64_t tok) {
   int s = 0;

@@ -7,15 +7,19 @@
 
 namespace sqg {
 
-enum { FMT_INT4 = 0, FMT_INT8 = 1 };
+enum { FMT_INT4 = 0, FMT_INT8 = 1, FMT_BF16 = 2 };
 
-// Token-range segments of the packed store (at most 16).
+// Token-range segments of the packed store (at most 16).  Within segment s, head h
+// uses format FMT_INT8 if fmt[s] is FMT_INT4 and bit h of int8_heads[s] is set, else
+// fmt[s]; its rows start at offset[s] + (end - begin) * (bytes of the rows of the
+// heads before it) and follow each other.
 struct SegTable {
   int32_t n;
   int32_t fmt[16];
   int64_t begin[16];
   int64_t end[16];
-  int64_t offset[16];   // byte offset of the segment in the packed store
+  int64_t offset[16];      // byte offset of the segment in the packed store
+  uint64_t int8_heads[16];
 };
 
 // One launch of the streamed QKV-quant kernel over rows [row_begin, row_end).

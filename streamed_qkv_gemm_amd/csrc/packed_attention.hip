@@ -73,6 +73,12 @@ __device__ __forceinline__ void dequant_int4x8(uint32_t w, uint32_t s2, uint32_t
   }
 }
 
+// two bf16 values (one dword) as two f16 values, each rounded to nearest
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  const f16x2 h = {(_Float16)__uint_as_float(w << 16), (_Float16)__uint_as_float(w & 0xffff0000u)};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 // 4 f16 values code * scale from 4 INT8 codes (one dword, code j in byte j)
 __device__ __forceinline__ void dequant_int8x4(uint32_t w, uint32_t s2, uint32_t (&out)[2]) {
   const uint32_t b = w ^ 0x80808080u;  // byte = code + 128
@@ -91,12 +97,14 @@ __device__ __forceinline__ void dequant_int8x4(uint32_t w, uint32_t s2, uint32_t
 // Packed codes and scales one thread moves per tile:
 //   K: one key, 16 dims (8 B INT4 in k[0..1], 16 B INT8 in k[0..3]) and its group scale;
 //   V: 4 keys x 4 dims (2 B INT4 or 4 B INT8 per key) and their scales.
+//   BF16 tiles are read later, in store_tile, from the tile's byte offset crow.
 struct TileRegs {
   u32x4 k;
   uint32_t kscale;
   uint32_t v[4];
   uint32_t vscale[4];
   int fmt;
+  uint32_t crow;
 };
 
 __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const AttnParams p) {
@@ -200,9 +208,9 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
       ++ld_seg;
       ld_sb = p.seg.begin[ld_seg];
       ld_se = p.seg.end[ld_seg];
-      ld_fmt = p.seg.fmt[ld_seg];
-      const int64_t rb = ld_fmt == FMT_INT4 ? 64 : 128;
-      const int64_t base = p.seg.offset[ld_seg] + (int64_t)head * (ld_se - ld_sb) * rb;
+      ld_fmt = head_format(p.seg, ld_seg, head);
+      const int64_t rb = format_row_bytes(ld_fmt);
+      const int64_t base = head_rows_offset(p.seg, ld_seg, head);
       const int32_t bytes = (int32_t)((ld_se - ld_sb) * rb);
       kr = __builtin_amdgcn_make_buffer_rsrc((void*)(p.kpack + base), 0, bytes, kBufferWord3);
       vr = __builtin_amdgcn_make_buffer_rsrc((void*)(p.vpack + base), 0, bytes, kBufferWord3);
@@ -212,7 +220,9 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
     r.kscale = __builtin_amdgcn_raw_buffer_load_b16(ksr, ks_off + srow, 0, 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) r.vscale[j] = __builtin_amdgcn_raw_buffer_load_b16(vsr, vs_off + srow + 8 * j, 0, 0);
-    if (ld_fmt == FMT_INT4) {
+    if (ld_fmt == FMT_BF16) {
+      r.crow = (uint32_t)((key0 - ld_sb) * 256);
+    } else if (ld_fmt == FMT_INT4) {
       const uint32_t crow = (uint32_t)((key0 - ld_sb) * 64);
       const u32x2 cw = __builtin_amdgcn_raw_buffer_load_b64(kr, k_off4 + crow, 0, 0);
       r.k[0] = cw[0];
@@ -245,13 +255,23 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
         o[i] = a[i];
         o[4 + i] = b[i];
       }
-    } else {
+    } else if (fmt == FMT_INT8) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         uint32_t cw[2];
         dequant_int8x4(r.k[w], ks2, cw);
         o[2 * w] = cw[0];
         o[2 * w + 1] = cw[1];
+      }
+    } else {
+      // bf16 rows, read now: bf16 -> fp32 is a shift, fp32 -> f16 rounds to nearest
+      // (exact for the 8 significant bits of bf16 within f16's normal range)
+      const u32x4 b0 = __builtin_amdgcn_raw_buffer_load_b128(kr, 256 * kkey + 32 * kpart + r.crow, 0, 0);
+      const u32x4 b1 = __builtin_amdgcn_raw_buffer_load_b128(kr, 256 * kkey + 32 * kpart + 16 + r.crow, 0, 0);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        o[w] = bf16x2_to_f16x2(b0[w]);
+        o[4 + w] = bf16x2_to_f16x2(b1[w]);
       }
     }
     u32x4 o0 = {o[0], o[1], o[2], o[3]};
@@ -266,11 +286,15 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
       uint32_t cw[4];
       if (fmt == FMT_INT4) {
         dequant_int4x8(r.v[j], s2, cw);   // codes 0..3 sit in the low 16 bits
-      } else {
+      } else if (fmt == FMT_INT8) {
         uint32_t c8[2];
         dequant_int8x4(r.v[j], s2, c8);
         cw[0] = c8[0];
         cw[1] = c8[1];
+      } else {
+        const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(vr, 256 * (4 * vq + j) + 8 * vd + r.crow, 0, 0);
+        cw[0] = bf16x2_to_f16x2(b[0]);
+        cw[1] = bf16x2_to_f16x2(b[1]);
       }
 #pragma unroll
       for (int e = 0; e < 2; ++e) {

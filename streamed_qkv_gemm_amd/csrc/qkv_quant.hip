@@ -228,9 +228,9 @@ __global__ __launch_bounds__(256, 1) void qkv_quant_kernel(const QkvParams p) {
   const int64_t wtok0 = tok0 + 128 * wt;
   if (wtok0 >= p.row_end) return;          // wave-uniform
   const int seg = find_segment(p.seg, wtok0);
-  const int fmt = p.seg.fmt[seg];
-  const int64_t seg_len = p.seg.end[seg] - p.seg.begin[seg];
-  const int row_bytes = (fmt == FMT_INT4) ? 64 : 128;
+  const int fmt = head_format(p.seg, seg, h);
+  const int64_t head_base = head_rows_offset(p.seg, seg, h);
+  const int row_bytes = format_row_bytes(fmt);
 
   // The token-block loop stays rolled (its body is large); the accumulator column
   // is picked with static indices so the accumulators never leave registers.
@@ -281,13 +281,14 @@ __global__ __launch_bounds__(256, 1) void qkv_quant_kernel(const QkvParams p) {
       uint8_t* store = (section == 1) ? p.kpack : p.vpack;
       uint16_t* scl = (section == 1) ? p.kscale : p.vscale;
       const int64_t tt = valid ? t : wtok0;
-      uint8_t* row = store + p.seg.offset[seg] +
-                     ((int64_t)h * seg_len + (tt - p.seg.begin[seg])) * row_bytes;
+      uint8_t* row = store + head_base + (tt - p.seg.begin[seg]) * row_bytes;
       uint16_t* srow = scl + ((int64_t)h * p.kv_n + (tt - p.kv_row0)) * 4;
       if (fmt == FMT_INT4)
         quant_pack_store<FMT_INT4>(u, row, srow, valid);
-      else
+      else if (fmt == FMT_INT8)
         quant_pack_store<FMT_INT8>(u, row, srow, valid);
+      else
+        bf16_row_store(u, row, srow, valid);
     }
   }
 }

@@ -51,11 +51,21 @@ std::vector<std::pair<int64_t, int64_t>> chunk_plan(int64_t n, int64_t size, int
   return out;
 }
 
+int format_row_bytes(int32_t fmt) { return fmt == SQG_INT4_ROT ? 64 : (fmt == SQG_INT8_ROT ? 128 : 256); }
+
+// Bytes of one token's rows over heads [0, h) of segment s: INT8 heads of an INT4
+// segment take 64 bytes more than the others.
+int64_t segment_row_units(const sqg_layout& L, int s, int h) {
+  const uint64_t below = h >= 64 ? L.seg_int8_heads[s] : (L.seg_int8_heads[s] & ((1ull << h) - 1ull));
+  return (int64_t)L.seg_row_bytes[s] * h + 64 * (int64_t)__builtin_popcountll(below);
+}
+
 int build_layout(int64_t n, int32_t d, int32_t heads, const sqg_range* ranges, int32_t n_ranges,
                  sqg_layout* L) {
   if (n < 0) return fail(SQG_ERR_INVALID_ARGUMENT, "n_tokens must be >= 0 (got %lld)", (long long)n);
   if (heads < 1 || d != heads * SQG_HEAD_DIM)
     return fail(SQG_ERR_INVALID_ARGUMENT, "d_model (%d) must equal 128 * n_heads (%d)", d, heads);
+  if (heads > 64) return fail(SQG_ERR_UNSUPPORTED, "at most 64 heads (got %d)", heads);
   if (n_ranges < 0 || n_ranges > SQG_MAX_SEGMENTS)
     return fail(SQG_ERR_INVALID_ARGUMENT, "n_ranges must be in [0, %d] (got %d)", SQG_MAX_SEGMENTS,
                 n_ranges);
@@ -74,9 +84,13 @@ int build_layout(int64_t n, int32_t d, int32_t heads, const sqg_range* ranges, i
     int64_t pos = 0;
     for (int i = 0; i < n_ranges; ++i) {
       const sqg_range& r = ranges[i];
-      if (r.fmt != SQG_INT4_ROT && r.fmt != SQG_INT8_ROT)
+      if (r.fmt != SQG_INT4_ROT && r.fmt != SQG_INT8_ROT && r.fmt != SQG_BF16_ROT)
         return fail(SQG_ERR_INVALID_ARGUMENT, "range %d: unknown format %d", i, r.fmt);
       if (r.reserved != 0) return fail(SQG_ERR_INVALID_ARGUMENT, "range %d: reserved field not 0", i);
+      if (r.int8_heads != 0 && r.fmt != SQG_INT4_ROT)
+        return fail(SQG_ERR_INVALID_ARGUMENT, "range %d: int8_heads applies to INT4 ranges only", i);
+      if (heads < 64 && (r.int8_heads >> heads) != 0)
+        return fail(SQG_ERR_INVALID_ARGUMENT, "range %d: int8_heads names a head >= n_heads", i);
       if (r.begin != pos)
         return fail(SQG_ERR_INVALID_ARGUMENT,
                     "range %d begins at %lld, expected %lld (ranges must be sorted and contiguous)",
@@ -89,6 +103,7 @@ int build_layout(int64_t n, int32_t d, int32_t heads, const sqg_range* ranges, i
       L->seg_begin[i] = r.begin;
       L->seg_end[i] = r.end;
       L->seg_fmt[i] = r.fmt;
+      L->seg_int8_heads[i] = r.int8_heads;
       pos = r.end;
     }
     if (pos != n)
@@ -98,9 +113,9 @@ int build_layout(int64_t n, int32_t d, int32_t heads, const sqg_range* ranges, i
   }
   int64_t off = 0;
   for (int s = 0; s < L->n_segments; ++s) {
-    L->seg_row_bytes[s] = L->seg_fmt[s] == SQG_INT4_ROT ? 64 : 128;
+    L->seg_row_bytes[s] = format_row_bytes(L->seg_fmt[s]);
     L->seg_offset[s] = off;
-    off += (int64_t)heads * (L->seg_end[s] - L->seg_begin[s]) * L->seg_row_bytes[s];
+    off += (L->seg_end[s] - L->seg_begin[s]) * segment_row_units(*L, s, heads);
   }
   L->pack_bytes = off;
   L->scale_bytes = n * heads * 4 * 2;
@@ -130,8 +145,9 @@ int build_block_layout(const sqg_layout& full, int32_t d, int64_t k0, int64_t k1
     B->seg_end[i] = e;
     B->seg_fmt[i] = full.seg_fmt[s];
     B->seg_row_bytes[i] = full.seg_row_bytes[s];
+    B->seg_int8_heads[i] = full.seg_int8_heads[s];
     B->seg_offset[i] = off;
-    off += (int64_t)full.n_heads * (e - b) * full.seg_row_bytes[s];
+    off += (e - b) * segment_row_units(full, s, full.n_heads);
   }
   B->pack_bytes = off;
   B->scale_bytes = B->n_tokens * full.n_heads * 4 * 2;
@@ -192,6 +208,7 @@ sqg::SegTable seg_table(const sqg_layout& L) {
     t.begin[s] = L.seg_begin[s];
     t.end[s] = L.seg_end[s];
     t.offset[s] = L.seg_offset[s];
+    t.int8_heads[s] = L.seg_int8_heads[s];
   }
   return t;
 }
@@ -425,6 +442,18 @@ SQG_API int sqg_kv_layout(int64_t n_tokens, int32_t d_model, int32_t n_heads,
   if (!out) return fail(SQG_ERR_INVALID_ARGUMENT, "out is NULL");
   const int st = build_layout(n_tokens, d_model, n_heads, ranges, n_ranges, out);
   return st == SQG_OK ? ok() : st;
+}
+
+SQG_API int64_t sqg_kv_row_offset(const sqg_layout* L, int32_t head, int64_t token) {
+  if (!L || head < 0 || head >= L->n_heads) return -1;
+  for (int s = 0; s < L->n_segments; ++s) {
+    if (token < L->seg_begin[s] || token >= L->seg_end[s]) continue;
+    const bool int8 = L->seg_fmt[s] == SQG_INT4_ROT && ((L->seg_int8_heads[s] >> head) & 1ull);
+    const int64_t rb = int8 ? 128 : L->seg_row_bytes[s];
+    return L->seg_offset[s] + (L->seg_end[s] - L->seg_begin[s]) * segment_row_units(*L, s, head) +
+           (token - L->seg_begin[s]) * rb;
+  }
+  return -1;
 }
 
 SQG_API int sqg_kv_block_layout(int64_t n_tokens, int32_t d_model, int32_t n_heads,

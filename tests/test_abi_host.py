@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 10
     for n in names:
         assert hasattr(lib, n), n
-    assert sqg.version() == 110
+    assert sqg.version() == 120
 
 
 def test_struct_sizes_match_binding():
@@ -70,13 +70,22 @@ def test_chunk_plan_random_matches_oracle():
     (152263, 7168, None),
     (1000, 512, [(0, 128, 1), (128, 1000, 0)]),
     (777, 256, [(0, 256, 0), (256, 384, 1), (384, 777, 0)]),
+    (2000, 768, [(0, 256, 2), (256, 640, 1), (640, 1536, 0, 0b100101), (1536, 2000, 2)]),
+    (65536, 7168, [(0, 512, 2), (512, 8704, 1), (8704, 65536, 0, (1 << 56) - 1 - (1 << 7))]),
 ])
 def test_layout_matches_oracle(n, d, ranges):
     L = sqg.kv_layout(n, d, ranges)
     segs = oracle.range_segments(n, ranges)
-    ol, total = oracle.packed_layout(n, d // 128, segs)
+    H = d // 128
+    ol, total = oracle.packed_layout(n, H, segs)
     assert L["pack_bytes"] == total
-    assert L["segments"] == ol
+    keys = ("begin", "end", "fmt", "int8_heads", "offset", "row_bytes")
+    assert [tuple(s[k] for k in keys) for s in L["segments"]] == [tuple(s[k] for k in keys) for s in ol]
+    for seg in ol:
+        for h in sorted({0, 1, H // 2, H - 1}):
+            for t in (seg["begin"], seg["end"] - 1):
+                want = seg["head_offset"][h] + (t - seg["begin"]) * seg["head_row_bytes"][h]
+                assert sqg.kv_row_offset(L, h, t) == want
     ws = oracle.working_set_bytes(n, d, segs)
     assert L["q_bytes"] == ws["q"] and L["bf16_qkv_bytes"] == ws["bf16_qkv"]
     assert L["scale_bytes"] == ws["k_scales"]
@@ -89,10 +98,14 @@ def test_layout_matches_oracle(n, d, ranges):
     [(0, 512, 7), (512, 1024, 0)],
     [(0, 512, 1), (512, 1000, 0)],
     [(128, 1024, 0)],
+    [(0, 512, 3), (512, 1024, 0)],                # unknown format
+    [(0, 512, 1, 1), (512, 1024, 0)],             # head mask on an INT8 range
+    [(0, 512, 2, 4), (512, 1024, 0)],             # head mask on a BF16 range
+    [(0, 512, 0, 1 << 4), (512, 1024, 0)],        # head 4 of 4
 ])
 def test_layout_rejects_bad_policies_like_the_oracle(ranges):
     with pytest.raises(ValueError):
-        oracle.range_segments(1024, ranges)
+        oracle.range_segments(1024, ranges, n_heads=4)
     with pytest.raises(sqg.SqgError) as e:
         sqg.kv_layout(1024, 512, ranges)
     assert e.value.status == -1

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synth
-from oracle import INT4, INT8
+from oracle import BF16, INT4, INT8
 
 pytestmark = pytest.mark.gpu
 
@@ -40,35 +40,44 @@ def block_rows_of(lib, staged, full_ranges):
     po = so = 0
     for k0, k1 in lib.chunk_ranges(N, staged["block_rows"], 512):
         L = lib.kv_block_layout(N, D, k0, k1, full_ranges)
-        lay = [dict(s, begin=s["begin"] - k0, end=s["end"] - k0) for s in L["segments"]]
+        # the oracle's layout of the clipped policy, in block coordinates
+        clipped = [(max(r[0], k0) - k0, min(r[1], k1) - k0) + tuple(r[2:])
+                   for r in full_ranges if min(r[1], k1) > max(r[0], k0)]
+        lay, total = oracle.packed_layout(k1 - k0, H, oracle.range_segments(k1 - k0, clipped))
+        assert total == L["pack_bytes"]
         rows = np.arange(k1 - k0)
         got = {}
         for t in ("k", "v"):
             pk = host(staged["host_%spack" % t])[po:po + L["pack_bytes"]]
             sc = host(staged["host_%sscale" % t])[so:so + L["scale_bytes"]].view(np.float16)
-            got[t] = oracle.gather_packed_rows(pk, sc.reshape(H, k1 - k0, 4), lay, H, rows)
+            got[t] = oracle.gather_packed_rows(pk, sc.reshape(H, k1 - k0, 4), lay, H, rows) + \
+                (oracle.gather_bf16_rows(pk, lay, H, rows),)
         out.append((k0, k1, got))
         po += L["pack_bytes"]
         so += L["scale_bytes"]
     return out
 
 
-@pytest.mark.parametrize("block", [512, 1024])
-def test_staged_store_holds_the_device_store_bytes(lib, block):
+MIXED = [(0, 256, BF16), (256, 640, INT8), (640, 2304, INT4, 0b1010), (2304, N, BF16)]
+
+
+@pytest.mark.parametrize("block,policy", [(512, POLICY), (1024, POLICY), (512, MIXED)])
+def test_staged_store_holds_the_device_store_bytes(lib, block, policy):
     H = D // 128
     x, w, kw = make(lib, 301)
-    full = lib.streamed_qkv_quant(x, w, ranges=POLICY, **kw)
-    staged = lib.alloc_staged(N, D, block, POLICY, device=DEV)
+    full = lib.streamed_qkv_quant(x, w, ranges=policy, **kw)
+    staged = lib.alloc_staged(N, D, block, policy, device=DEV)
     q = lib.streamed_qkv_quant_staged(x, w, staged, **kw)
     torch.cuda.synchronize()
     assert torch.equal(q, full["q"])
-    layout, _ = oracle.packed_layout(N, H, oracle.range_segments(N, POLICY))
-    for k0, k1, got in block_rows_of(lib, staged, POLICY):
+    layout, _ = oracle.packed_layout(N, H, oracle.range_segments(N, policy))
+    for k0, k1, got in block_rows_of(lib, staged, policy):
         rows = np.arange(k0, k1)
         for t in ("k", "v"):
             want = oracle.gather_packed_rows(host(full[t + "pack"]), host(full[t + "scale"]), layout, H, rows)
             assert np.array_equal(got[t][0], want[0]), (t, k0)
             assert np.array_equal(got[t][1].view(np.uint16), want[1].view(np.uint16)), (t, k0)
+            assert np.array_equal(got[t][2], oracle.gather_bf16_rows(host(full[t + "pack"]), layout, H, rows))
 
 
 def test_staged_kv_only_build_matches(lib):
@@ -83,11 +92,11 @@ def test_staged_kv_only_build_matches(lib):
         assert torch.equal(a[k], b[k]), k
 
 
-@pytest.mark.parametrize("block", [512, 1024])
-def test_staged_attention_equals_device_blocks(lib, block):
+@pytest.mark.parametrize("block,policy", [(512, POLICY), (1024, POLICY), (1024, MIXED)])
+def test_staged_attention_equals_device_blocks(lib, block, policy):
     x, w, kw = make(lib, 321)
-    full = lib.streamed_qkv_quant(x, w, ranges=POLICY, **kw)
-    staged = lib.alloc_staged(N, D, block, POLICY, device=DEV)
+    full = lib.streamed_qkv_quant(x, w, ranges=policy, **kw)
+    staged = lib.alloc_staged(N, D, block, policy, device=DEV)
     lib.streamed_qkv_quant_staged(x, w, staged, emit=lib.SQG_EMIT_KV, **kw)
     o_ref, l_ref = lib.packed_kv_attention(full, kv_block=block)
     o, l = lib.packed_kv_attention_staged(staged, full["q"])
@@ -95,7 +104,7 @@ def test_staged_attention_equals_device_blocks(lib, block):
     assert torch.equal(o, o_ref) and torch.equal(l, l_ref)
     # G3 on its own against the oracle, sampled rows
     H = D // 128
-    layout, _ = oracle.packed_layout(N, H, oracle.range_segments(N, POLICY))
+    layout, _ = oracle.packed_layout(N, H, oracle.range_segments(N, policy))
     rows = np.arange(0, N, 29)
     want, lse_want = oracle.attention_rows_from_store(
         synth.bf16_bits(full["q"])[rows], rows, host(full["kpack"]), host(full["vpack"]),
