@@ -36,8 +36,8 @@ MEASURED_TRAFFIC = {
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
@@ -130,6 +130,8 @@ def main():
     qkv_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     att_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     step_ms = sum(e[0].elapsed_time(e[2]) for e in evs) / args.steps
+    step_ms_sorted = sorted(e[0].elapsed_time(e[2]) for e in evs)
+    step_ms_median = step_ms_sorted[len(step_ms_sorted) // 2]
 
     qkv_flop = 2.0 * N * d * 3 * d
     att_flop = 4.0 * N * N * H * 128
@@ -248,6 +250,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": step_ms,
+        "ms_per_step_median": step_ms_median,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -18,9 +18,11 @@
 //
 // Workgroup: 256 queries of one head, eight waves of 32 queries (two waves per
 // SIMD, so one wave's softmax and dequantisation overlap the other's MFMAs).
-// Per 64-key tile the workgroup loads the packed codes and fp16 scales once,
-// dequantises them to f16 in LDS (K row-major, V transposed), and every wave
-// computes
+// Per 64-key tile the workgroup loads the packed codes and fp16 scales once (waves
+// 0-3 the K codes, waves 4-7 the V codes: one 32-value group of one key per thread,
+// one code load and one scale load), dequantises them to f16 in LDS (K and V both
+// row-major; the P.V operands come out of LDS through transposing reads), and
+// every wave computes
 //   S^T = K_r Q_r^T        (keys x queries, 32x32x16 f16 MFMA)
 //   online softmax down each query column (one lane-pair exchange per tile)
 //   O^T += V_r^T P^T       (dims x queries)
@@ -44,16 +46,10 @@ constexpr int kBQ = 32 * kWaves;      // queries per workgroup
 constexpr int kBKV = 64;              // keys per tile
 constexpr int kKB = kBKV / 32;        // 32-key MFMA blocks per tile
 constexpr int kKStride = 128 + 8;     // f16 per K row in LDS (272 B)
-constexpr int kVStride = kBKV + 8;    // f16 per transposed V row in LDS (144 B)
 constexpr int kKTile = kBKV * kKStride;
-constexpr int kVTile = 128 * kVStride;
+constexpr int kVTile = kBKV * kKStride;  // V row-major like K
 constexpr float kRescaleLog2 = 8.0f;  // move the running max only past this growth
 
-// position of key k (0..kBKV-1) inside a transposed V row: bits 2 and 3 are swapped
-// so that the 8 keys one lane feeds to a 16-key MFMA step are contiguous
-__device__ __forceinline__ int vpos(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
 
 // 8 f16 values code * scale from 8 INT4 codes (one dword, code j in bits 4j..4j+3)
 __device__ __forceinline__ void dequant_int4x8(uint32_t w, uint32_t s2, uint32_t (&out)[4]) {
@@ -71,6 +67,15 @@ __device__ __forceinline__ void dequant_int4x8(uint32_t w, uint32_t s2, uint32_t
     v = v * sc;                                       // exact: the scale has few bits
     out[p] = __builtin_bit_cast(uint32_t, v);
   }
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, lane c
+// supplies the address of 4 consecutive f16 values (chunk c) and lane i receives
+// element i % 4 of chunks i / 4 + 4 j, j = 0..3.
+__device__ __forceinline__ f16x4 tr_read_f16x4(const _Float16* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
+  return __builtin_bit_cast(f16x4, r);
 }
 
 // two bf16 values (one dword) as two f16 values, each rounded to nearest
@@ -94,15 +99,12 @@ __device__ __forceinline__ void dequant_int8x4(uint32_t w, uint32_t s2, uint32_t
   }
 }
 
-// Packed codes and scales one thread moves per tile:
-//   K: one key, 16 dims (8 B INT4 in k[0..1], 16 B INT8 in k[0..3]) and its group scale;
-//   V: 4 keys x 4 dims (2 B INT4 or 4 B INT8 per key) and their scales.
-//   BF16 tiles are read later, in store_tile, from the tile's byte offset crow.
+// Packed codes and the group scale one thread moves per tile: 32 values of one key
+// (16 B INT4 in c0, 32 B INT8 in c0, c1); BF16 tiles are read later, in store_tile,
+// from the tile's byte offset crow.
 struct TileRegs {
-  u32x4 k;
-  uint32_t kscale;
-  uint32_t v[4];
-  uint32_t vscale[4];
+  u32x4 c0, c1;
+  uint32_t scale;
   int fmt;
   uint32_t crow;
 };
@@ -177,32 +179,29 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
   }
   const _Float16* qlw = sQl[wave];
 
-  // ---- per-thread maps for the K/V tile loads (64 keys per tile, 512 threads)
-  const int kkey = tid >> 3;   // K: key of the tile, dims 16 kpart .. + 15
-  const int kpart = tid & 7;
-  const int vq = tid & 15;     // V: keys 4 vq .. 4 vq + 3, dims 4 vd .. 4 vd + 3
-  const int vd = tid >> 4;
-
-  // per-thread byte offsets inside a tile (same for every tile of a format)
-  const uint32_t k_off4 = (uint32_t)(kkey * 64 + 8 * kpart);
-  const uint32_t k_off8 = (uint32_t)(kkey * 128 + 16 * kpart);
-  const uint32_t ks_off = (uint32_t)(2 * (kkey * 4 + (kpart >> 1)));
-  const uint32_t v_off4 = (uint32_t)(4 * vq * 64 + 2 * vd);
-  const uint32_t v_off8 = (uint32_t)(4 * vq * 128 + 4 * vd);
-  const uint32_t vs_off = (uint32_t)(2 * (4 * vq * 4 + (vd >> 3)));
+  // ---- per-thread maps for the K/V tile loads (64 keys per tile, 512 threads): waves
+  // 0-3 bring K, waves 4-7 bring V; thread (key, grp) moves group grp (32 values) of one
+  // key: one code load and one scale load per tile.
+  const bool vside = wave >= kWaves / 2;   // wave-uniform
+  const int tkey = (tid & 255) >> 2;
+  const int tgrp = tid & 3;
+  const uint32_t c_off4 = (uint32_t)(tkey * 64 + 16 * tgrp);
+  const uint32_t c_off8 = (uint32_t)(tkey * 128 + 32 * tgrp);
+  const uint32_t c_off16 = (uint32_t)(tkey * 256 + 64 * tgrp);
+  const uint32_t s_off = (uint32_t)(2 * (tkey * 4 + tgrp));
 
   // Tile loads go through buffer resources that cover this head's rows of one
   // segment (codes) or of the whole sequence (scales); rows past the end read as
   // zero.  The load cursor below follows the segment of the next tile to load in
   // scalar registers, so a tile costs a few scalar adds and one vector add per base.
-  const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.kscale + (int64_t)head * p.kv_n * 4), 0, (int32_t)(p.kv_n * 8), kBufferWord3);
-  const __amdgpu_buffer_rsrc_t vsr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.vscale + (int64_t)head * p.kv_n * 4), 0, (int32_t)(p.kv_n * 8), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((vside ? p.vscale : p.kscale) + (int64_t)head * p.kv_n * 4), 0, (int32_t)(p.kv_n * 8),
+      kBufferWord3);
+  const uint8_t* const cbase = vside ? p.vpack : p.kpack;
   int ld_seg = -1;
   int64_t ld_sb = 0, ld_se = 0;
   int ld_fmt = FMT_INT4;
-  __amdgpu_buffer_rsrc_t kr = ksr, vr = vsr;
+  __amdgpu_buffer_rsrc_t cr = sr;
   auto load_tile = [&](int64_t key0, TileRegs& r) {
     while (key0 >= ld_se) {  // the tile starts a new segment (rare)
       ++ld_seg;
@@ -212,102 +211,58 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
       const int64_t rb = format_row_bytes(ld_fmt);
       const int64_t base = head_rows_offset(p.seg, ld_seg, head);
       const int32_t bytes = (int32_t)((ld_se - ld_sb) * rb);
-      kr = __builtin_amdgcn_make_buffer_rsrc((void*)(p.kpack + base), 0, bytes, kBufferWord3);
-      vr = __builtin_amdgcn_make_buffer_rsrc((void*)(p.vpack + base), 0, bytes, kBufferWord3);
+      cr = __builtin_amdgcn_make_buffer_rsrc((void*)(cbase + base), 0, bytes, kBufferWord3);
     }
-    const uint32_t srow = (uint32_t)((key0 - p.kv_row0) * 8);
     r.fmt = ld_fmt;
-    r.kscale = __builtin_amdgcn_raw_buffer_load_b16(ksr, ks_off + srow, 0, 0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r.vscale[j] = __builtin_amdgcn_raw_buffer_load_b16(vsr, vs_off + srow + 8 * j, 0, 0);
-    if (ld_fmt == FMT_BF16) {
-      r.crow = (uint32_t)((key0 - ld_sb) * 256);
-    } else if (ld_fmt == FMT_INT4) {
-      const uint32_t crow = (uint32_t)((key0 - ld_sb) * 64);
-      const u32x2 cw = __builtin_amdgcn_raw_buffer_load_b64(kr, k_off4 + crow, 0, 0);
-      r.k[0] = cw[0];
-      r.k[1] = cw[1];
-      r.k[2] = 0u;
-      r.k[3] = 0u;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) r.v[j] = __builtin_amdgcn_raw_buffer_load_b16(vr, v_off4 + crow + 64 * j, 0, 0);
-    } else {
+    r.scale = __builtin_amdgcn_raw_buffer_load_b16(sr, s_off + (uint32_t)((key0 - p.kv_row0) * 8), 0, 0);
+    if (ld_fmt == FMT_INT4) {
+      r.c0 = __builtin_amdgcn_raw_buffer_load_b128(cr, c_off4 + (uint32_t)((key0 - ld_sb) * 64), 0, 0);
+    } else if (ld_fmt == FMT_INT8) {
       const uint32_t crow = (uint32_t)((key0 - ld_sb) * 128);
-      r.k = __builtin_amdgcn_raw_buffer_load_b128(kr, k_off8 + crow, 0, 0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) r.v[j] = __builtin_amdgcn_raw_buffer_load_b32(vr, v_off8 + crow + 128 * j, 0, 0);
+      r.c0 = __builtin_amdgcn_raw_buffer_load_b128(cr, c_off8 + crow, 0, 0);
+      r.c1 = __builtin_amdgcn_raw_buffer_load_b128(cr, c_off8 + crow + 16, 0, 0);
+    } else {
+      r.crow = (uint32_t)((key0 - ld_sb) * 256);
     }
   };
 
+  // decode one thread's 32 values into row tkey, elements 32 tgrp .. + 31, of the K or V
+  // tile (both row-major: key rows of 128 dims)
   auto store_tile = [&](const TileRegs& r, int stage) {
-    _Float16* K = sK[stage];
-    _Float16* V = sV[stage];
+    _Float16* dst = (vside ? sV[stage] : sK[stage]) + tkey * kKStride + 32 * tgrp;
     const int fmt = __builtin_amdgcn_readfirstlane(r.fmt);
-    const uint32_t ks2 = r.kscale | (r.kscale << 16);
-    // K: 16 values of (key, part) -> row kkey, elements 16 kpart ..
-    uint32_t o[8];
+    const uint32_t s2 = r.scale | (r.scale << 16);
+    uint32_t o[16];
     if (fmt == FMT_INT4) {
-      uint32_t a[4], b[4];
-      dequant_int4x8(r.k[0], ks2, a);
-      dequant_int4x8(r.k[1], ks2, b);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        o[i] = a[i];
-        o[4 + i] = b[i];
+      for (int w = 0; w < 4; ++w) {
+        uint32_t a[4];
+        dequant_int4x8(r.c0[w], s2, a);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[4 * w + i] = a[i];
       }
     } else if (fmt == FMT_INT8) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t cw[2];
-        dequant_int8x4(r.k[w], ks2, cw);
-        o[2 * w] = cw[0];
-        o[2 * w + 1] = cw[1];
+      for (int w = 0; w < 8; ++w) {
+        uint32_t a[2];
+        dequant_int8x4(w < 4 ? r.c0[w] : r.c1[w - 4], s2, a);
+        o[2 * w] = a[0];
+        o[2 * w + 1] = a[1];
       }
     } else {
       // bf16 rows, read now: bf16 -> fp32 is a shift, fp32 -> f16 rounds to nearest
       // (exact for the 8 significant bits of bf16 within f16's normal range)
-      const u32x4 b0 = __builtin_amdgcn_raw_buffer_load_b128(kr, 256 * kkey + 32 * kpart + r.crow, 0, 0);
-      const u32x4 b1 = __builtin_amdgcn_raw_buffer_load_b128(kr, 256 * kkey + 32 * kpart + 16 + r.crow, 0, 0);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        o[w] = bf16x2_to_f16x2(b0[w]);
-        o[4 + w] = bf16x2_to_f16x2(b1[w]);
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(cr, c_off16 + r.crow + 16 * i, 0, 0);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) o[4 * i + w] = bf16x2_to_f16x2(b[w]);
       }
     }
-    u32x4 o0 = {o[0], o[1], o[2], o[3]};
-    u32x4 o1 = {o[4], o[5], o[6], o[7]};
-    *reinterpret_cast<u32x4*>(K + kkey * kKStride + 16 * kpart) = o0;
-    *reinterpret_cast<u32x4*>(K + kkey * kKStride + 16 * kpart + 8) = o1;
-    // V: 4 keys x 4 dims, written transposed: row = dim, the 4 keys contiguous
-    _Float16 vals[4][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t s2 = r.vscale[j] | (r.vscale[j] << 16);
-      uint32_t cw[4];
-      if (fmt == FMT_INT4) {
-        dequant_int4x8(r.v[j], s2, cw);   // codes 0..3 sit in the low 16 bits
-      } else if (fmt == FMT_INT8) {
-        uint32_t c8[2];
-        dequant_int8x4(r.v[j], s2, c8);
-        cw[0] = c8[0];
-        cw[1] = c8[1];
-      } else {
-        const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(vr, 256 * (4 * vq + j) + 8 * vd + r.crow, 0, 0);
-        cw[0] = bf16x2_to_f16x2(b[0]);
-        cw[1] = bf16x2_to_f16x2(b[1]);
-      }
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const f16x2 h2 = __builtin_bit_cast(f16x2, cw[e]);
-        vals[j][2 * e] = h2[0];
-        vals[j][2 * e + 1] = h2[1];
-      }
-    }
-    const int pos = vpos(4 * vq);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      f16x4 col = {vals[0][e], vals[1][e], vals[2][e], vals[3][e]};
-      *reinterpret_cast<f16x4*>(V + (4 * vd + e) * kVStride + pos) = col;
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 v = {o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+      *reinterpret_cast<u32x4*>(dst + 8 * i) = v;
     }
   };
 
@@ -409,10 +364,19 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
   auto do_pv = [&](int stage, const f16x8 (&pf)[2 * kKB]) {
     const _Float16* V = sV[stage];
     f16x8 vf[2][4];
+    // A operand (V^T) by transposing LDS reads: lane L gets dim 32 db + L % 32 of keys
+    // 16 ks + 4 hsel + 0..3 and 16 ks + 8 + 4 hsel + 0..3 (the MFMA's k slots 8 hsel + e
+    // with bits 2 and 3 swapped, matching the key order of the P operand).  Each 16-lane
+    // group reads 4 keys x 16 dims: lane c points at key (c / 4), dims 4 (c % 4) .. + 3.
+    const _Float16* vbase = V + (4 * hsel + ((lane & 15) >> 2)) * kKStride + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     auto rd = [&](int ks, int b) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-        vf[b][db] = *reinterpret_cast<const f16x8*>(V + (32 * db + l32) * kVStride + 16 * ks + 8 * hsel);
+      for (int db = 0; db < 4; ++db) {
+        const _Float16* a = vbase + 16 * ks * kKStride + 32 * db;
+        const f16x4 lo = tr_read_f16x4(a);
+        const f16x4 hi = tr_read_f16x4(a + 8 * kKStride);
+        vf[b][db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
     };
     rd(0, 0);
     __builtin_amdgcn_sched_barrier(0);
