@@ -28,6 +28,8 @@ __all__ = [
     "softmax_attention", "online_merge", "attention_blockwise",
     "attention_rotated_rows", "attention_model_rows", "attention_rows_from_store",
     "working_set_bytes", "quality_vs_unquantised",
+    "E4M3_MAX", "f32_to_e4m3", "e4m3_to_f64", "e8m0_exponent", "fp8_block_quantize",
+    "fp8_block_dequantize", "attention_fp8qk_rotated",
 ]
 
 HEAD_DIM = 128          # head dimension of every workload ([VL] docstring: 7168 = 56 x 128)
@@ -525,12 +527,13 @@ def attention_rows_from_store(q_bits: np.ndarray, rows: np.ndarray, kpack, vpack
                               vscale, layout, n_heads: int, n_tokens: int,
                               scale: Optional[float] = None, kv_block: int = 0,
                               kv_begin: int = 0, kv_end: Optional[int] = None,
-                              heads: Optional[Sequence[int]] = None):
+                              heads: Optional[Sequence[int]] = None, qk: str = "exact"):
     """Packed-K/V attention for the query rows `rows` against keys [kv_begin, kv_end).
 
     q_bits is [R, d] bf16 bits of those rows (model basis).  [FR] "Dense fallback
     is important": keys are decoded from the packed store (here: head by head, in
-    float64), never from a bf16 K/V.  Returns o [R, d] and lse [H, R]."""
+    float64), never from a bf16 K/V.  qk = "fp8" takes the scores on block-scaled
+    fp8 operands (`attention_fp8qk_rotated`).  Returns o [R, d] and lse [H, R]."""
     if scale is None:
         scale = HEAD_DIM ** -0.5
     if kv_end is None:
@@ -543,10 +546,98 @@ def attention_rows_from_store(q_bits: np.ndarray, rows: np.ndarray, kpack, vpack
         kr = decode_head(kpack, kscale, layout, n_heads, h, kv_begin, kv_end)
         vr = decode_head(vpack, vscale, layout, n_heads, h, kv_begin, kv_end)
         qh = q_bits[:, h * HEAD_DIM:(h + 1) * HEAD_DIM]
-        oh, lh = attention_rotated_rows(qh, kr, vr, scale, kv_block)
+        if qk == "fp8":
+            R = rotation_matrix(HEAD_DIM)
+            qr = (bf16_bits_to_f64(qh) @ R).astype(np.float32)
+            o_r, lh = attention_fp8qk_rotated(qr, kr, vr, scale, kv_block)
+            oh = o_r @ R.T
+        else:
+            oh, lh = attention_rotated_rows(qh, kr, vr, scale, kv_block)
         o[:, h * HEAD_DIM:(h + 1) * HEAD_DIM] = oh
         lse[h] = lh
     return o, lse
+
+
+# --------------------------------------------------------------------------- low-precision QK^T tier
+E4M3_MAX = 448.0
+
+
+def f32_to_e4m3(x) -> np.ndarray:
+    """OCP FP8 E4M3 code of each value: sign bit, 4-bit exponent with bias 7, 3-bit
+    mantissa, subnormals below 2^-6 in steps of 2^-9, no infinities, largest finite
+    value 448 (code 0x7e); round to nearest, ties to even; magnitudes above 448
+    saturate to 448.  Inputs are finite fp32 values (exact in float64)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    f, E = np.frexp(a)                        # a = f * 2^E, f in [0.5, 1)
+    e = np.maximum(np.where(a > 0, E - 1, -6), -6)   # binade of a (subnormals share -6)
+    step = np.ldexp(1.0, e - 3)              # spacing of the 3-bit mantissa
+    v = np.minimum(np.rint(a / step) * step, E4M3_MAX)   # rint: half to even
+    f2, E2 = np.frexp(v)
+    ev = E2 - 1
+    normal = v >= 2.0 ** -6
+    exp_field = np.where(normal, ev + 7, 0)
+    mant = np.where(normal, np.rint((v / np.ldexp(1.0, ev) - 1.0) * 8), np.rint(v / 2.0 ** -9))
+    code = (exp_field.astype(np.int64) << 3) | mant.astype(np.int64)
+    code = np.where(np.signbit(x), code | 0x80, code)
+    return code.astype(np.uint8)
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Value of each OCP FP8 E4M3 code (NaN for 0x7f and 0xff)."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    ef = (c >> 3) & 0xF
+    m = c & 7
+    mag = np.where(ef == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.ldexp(1.0, ef - 7))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def e8m0_exponent(amax) -> np.ndarray:
+    """Power-of-two block scale exponent: the smallest e with amax <= 448 * 2^e, so the
+    block's largest magnitude lands in (224, 448] after division by 2^e; clamped to
+    [-127, 127] (the E8M0 range); e = -127 for an all-zero block."""
+    a = np.asarray(amax, dtype=np.float64)
+    f, E = np.frexp(a)                       # a = f * 2^E; 448 = 0.875 * 2^9
+    e = np.where(f <= 0.875, E - 9, E - 8)
+    e = np.where(a > 0, e, -127)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def fp8_block_quantize(r: np.ndarray):
+    """MX-style fp8 of rotated vectors [..., 128]: per group of 32 values an E8M0
+    exponent e (`e8m0_exponent` of the group's max |r|) and the E4M3 codes of r / 2^e.
+    Returns (codes uint8 [..., 128], exponents int64 [..., 4])."""
+    r = np.asarray(r, dtype=np.float64)
+    g = r.reshape(r.shape[:-1] + (HEAD_DIM // GROUP, GROUP))
+    e = e8m0_exponent(np.max(np.abs(g), axis=-1))
+    codes = f32_to_e4m3(g / np.ldexp(1.0, e)[..., None])
+    return codes.reshape(r.shape), e
+
+
+def fp8_block_dequantize(codes: np.ndarray, exps: np.ndarray) -> np.ndarray:
+    c = e4m3_to_f64(codes)
+    g = c.reshape(c.shape[:-1] + (HEAD_DIM // GROUP, GROUP))
+    return (g * np.ldexp(1.0, np.asarray(exps))[..., None]).reshape(c.shape)
+
+
+def attention_fp8qk_rotated(q_rot: np.ndarray, k_rot: np.ndarray, v_rot: np.ndarray,
+                            scale: float, kv_block: int = 0):
+    """Attention with the scores taken on block-scaled fp8 operands, in the rotated
+    basis.  Reading of [VL] kvi8s section (an approximation tier: Hadamard-rotated Q
+    and K, QK^T on low-precision tensor cores straight from the store, no dequantised
+    K) carried to the MX formats of the MFMA unit: the rotated query (fp32) and the
+    decoded rotated keys are each quantised by `fp8_block_quantize` (one E8M0
+    exponent per group of 32 dims, E4M3 values); the scores are the exact dot
+    products of the dequantised operands; softmax, P.V with the decoded V, and the
+    KV-block merge are as in the exact tier.  Returns o [R, 128] in the rotated basis
+    and lse [R]."""
+    qd = fp8_block_dequantize(*fp8_block_quantize(np.asarray(q_rot, dtype=np.float32)))
+    kd = fp8_block_dequantize(*fp8_block_quantize(k_rot))
+    if kv_block and kv_block > 0:
+        return attention_blockwise(qd, kd, v_rot, scale, kv_block)
+    return softmax_attention(qd, kd, v_rot, scale)
 
 
 # --------------------------------------------------------------------------- memory
