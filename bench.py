@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--qrecompute-steps", type=int, default=1,
                     help="steps of the Q-recompute variant timed after the main steps (0 = skip)")
     ap.add_argument("--q-chunk-rows", type=int, default=0, help="query chunk of the Q-recompute variant")
+    ap.add_argument("--fp8-steps", type=int, default=1,
+                    help="steps of the fp8-QK attention tier timed after the main steps (0 = skip)")
     ap.add_argument("--staged-steps", type=int, default=1,
                     help="steps of the host-staged K/V variant timed after the main steps (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -141,6 +143,31 @@ def main():
     packed_ws = L["q_bytes"] + 2 * L["pack_bytes"] + 2 * L["scale_bytes"]
     att_tflops = att_flop / (att_ms * 1e-3) / 1e12
     qkv_tflops = qkv_flop / (qkv_ms * 1e-3) / 1e12
+
+    # ---- low-precision QK^T tier: the same attention with scores on block-scaled fp8
+    # operands (timed separately, not part of value; its output is compared with the
+    # exact tier's O of the last timed step)
+    fp8_res = None
+    if args.fp8_steps > 0:
+        o8 = torch.empty_like(o)
+        l8 = torch.empty_like(lse)
+        sqg.packed_kv_attention(store, kv_block=wl.kv_block, o=o8, lse=l8, qk_mode=sqg.SQG_QK_FP8)
+        torch.cuda.synchronize()
+        fe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.fp8_steps)]
+        for e0, e1 in fe:
+            e0.record(stream)
+            sqg.packed_kv_attention(store, kv_block=wl.kv_block, o=o8, lse=l8, qk_mode=sqg.SQG_QK_FP8)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        f_ms = sum(a.elapsed_time(b) for a, b in fe) / args.fp8_steps
+        rel = float(torch.linalg.vector_norm(o8 - o) / torch.linalg.vector_norm(o))
+        fp8_res = {"steps": args.fp8_steps, "attention_ms": f_ms,
+                   "attention_tflops": att_flop / (f_ms * 1e-3) / 1e12,
+                   "speedup_vs_exact_tier": att_ms / f_ms, "rel_l2_vs_exact_tier": rel,
+                   "dtype": "fp8 e4m3 QK^T (E8M0 per 32 dims), f16 P.V"}
+        del o8, l8
+        torch.cuda.empty_cache()
 
     # ---- Q-recompute variant: K/V-only projection, then Q rebuilt per query chunk inside
     # the attention call; no [N, d] Q buffer exists (timed separately, not part of value)
@@ -273,6 +300,7 @@ def main():
         "working_set_ratio": packed_ws / L["bf16_qkv_bytes"],
         "bf16_materialising_baseline": bf16_base,
         "qrecompute": qrec,
+        "fp8_qk_tier": fp8_res,
         "host_staged": staged_res,
         "wall_s_timed": wall,
         "roofline": {

@@ -36,7 +36,7 @@ extern "C" {
 #define SQG_API
 #endif
 
-#define SQG_VERSION 120          /* 1.2.0 */
+#define SQG_VERSION 130          /* 1.3.0 */
 #define SQG_HEAD_DIM 128
 #define SQG_GROUP 32
 #define SQG_MAX_SEGMENTS 16
@@ -64,6 +64,17 @@ typedef enum sqg_kv_format {
 } sqg_kv_format;
 
 typedef enum sqg_out_dtype { SQG_F32 = 0, SQG_BF16 = 1, SQG_F16 = 2 } sqg_out_dtype;
+
+/* Precision of the scores QK^T in attention.
+ * SQG_QK_EXACT: the rotated query as an f16 high part plus an f16 remainder against
+ *   the exactly dequantised f16 keys (two f16 MFMAs per step; the parity tier).
+ * SQG_QK_FP8: [VL] kvi8s section (an approximation tier: rotated Q and K, QK^T on
+ *   low-precision matrix cores straight from the store).  The rotated query and the
+ *   decoded keys are quantised per group of 32 dims to OCP E4M3 values with one E8M0
+ *   exponent (the smallest e with max |x| <= 448 * 2^e); the scores are the
+ *   block-scaled fp8 MFMA of those operands.  P.V is unchanged (f16).  Not bit-equal
+ *   to the exact tier. */
+typedef enum sqg_qk_mode { SQG_QK_EXACT = 0, SQG_QK_FP8 = 1 } sqg_qk_mode;
 
 /* What one sqg_streamed_qkv_quant call writes.  [VL] block section (the three-phase
  * streamed block): phase 1 keeps only K and V for the whole sequence and phase 2
@@ -167,6 +178,8 @@ typedef struct sqg_attn_args {
   int64_t ldo;
   float* lse;                  /* device, fp32 [H, N] natural-log LSE out, or NULL;
                                   required when accumulate or kv_block > 0 */
+  int32_t qk_mode;             /* sqg_qk_mode (0 = exact tier) */
+  int32_t reserved;            /* must be 0 */
 } sqg_attn_args;
 
 /* A K/V store held in host memory as consecutive block stores ([VL] module docstring:

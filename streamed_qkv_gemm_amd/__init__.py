@@ -6,7 +6,7 @@ tensors for device memory and the current HIP stream.  Build the library with
 `python -m streamed_qkv_gemm_amd.build` before use.
 """
 from ._binding import (  # noqa: F401
-    HEAD_DIM, LIB_PATH, SQG_BF16, SQG_EMIT_KV, SQG_EMIT_Q, SQG_EMIT_QKV, SQG_F16, SQG_F32,
+    HEAD_DIM, LIB_PATH, SQG_BF16, SQG_EMIT_KV, SQG_EMIT_Q, SQG_EMIT_QKV, SQG_F16, SQG_F32, SQG_QK_EXACT, SQG_QK_FP8,
     SQG_BF16_ROT, SQG_INT4_ROT, SQG_INT8_ROT, SqgError, alloc_store, chunk_ranges, kv_layout, lib_path, load,
     alloc_staged, kv_block_layout, kv_row_offset, packed_kv_attention, packed_kv_attention_qrecompute,
     packed_kv_attention_staged, qrecompute_workspace_bytes, rope_table, staged_sizes,

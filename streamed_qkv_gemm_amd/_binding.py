@@ -21,6 +21,7 @@ SQG_INT8_ROT = 1
 SQG_BF16_ROT = 2
 SQG_F32, SQG_BF16, SQG_F16 = 0, 1, 2
 SQG_EMIT_QKV, SQG_EMIT_Q, SQG_EMIT_KV = 0, 1, 2
+SQG_QK_EXACT, SQG_QK_FP8 = 0, 1
 MAX_SEGMENTS = 16
 HEAD_DIM = 128
 
@@ -67,7 +68,8 @@ class AttnArgs(ctypes.Structure):
                 ("ranges", ctypes.POINTER(Range)), ("n_ranges", _c_i32), ("o_dtype", _c_i32),
                 ("q_begin", _c_i64), ("q_end", _c_i64), ("kv_begin", _c_i64), ("kv_end", _c_i64),
                 ("kv_block", _c_i64), ("accumulate", _c_i32), ("softmax_scale", ctypes.c_float),
-                ("o", _vp), ("ldo", _c_i64), ("lse", _vp)]
+                ("o", _vp), ("ldo", _c_i64), ("lse", _vp), ("qk_mode", _c_i32),
+                ("reserved", _c_i32)]
 
 
 class StagedKV(ctypes.Structure):
@@ -282,7 +284,7 @@ _ODT = {torch.float32: SQG_F32, torch.bfloat16: SQG_BF16, torch.float16: SQG_F16
 
 
 def _attn_args(store: Dict, N: int, d: int, device, q_begin, q_end, kv_begin, kv_end, kv_block,
-               accumulate, o, lse, o_dtype, softmax_scale, want_lse):
+               accumulate, o, lse, o_dtype, softmax_scale, want_lse, qk_mode=SQG_QK_EXACT):
     H = d // HEAD_DIM
     if o is None:
         o = torch.empty((N, d), dtype=o_dtype, device=device)
@@ -300,6 +302,7 @@ def _attn_args(store: Dict, N: int, d: int, device, q_begin, q_end, kv_begin, kv
     a.kv_block, a.accumulate, a.softmax_scale = kv_block, int(bool(accumulate)), softmax_scale
     a.o, a.ldo = _dev_ptr(o, "o"), o.stride(0)
     a.lse = _dev_ptr(lse, "lse")
+    a.qk_mode, a.reserved = qk_mode, 0
     # keep the ranges array alive as long as the struct
     return a, arr, o, lse
 
@@ -308,18 +311,20 @@ def packed_kv_attention(store: Dict, q: Optional[torch.Tensor] = None, q_begin: 
                         q_end: int = 0, kv_begin: int = 0, kv_end: int = 0, kv_block: int = 0,
                         accumulate: bool = False, o: Optional[torch.Tensor] = None,
                         lse: Optional[torch.Tensor] = None, o_dtype=torch.float32,
-                        softmax_scale: float = 0.0, want_lse: bool = True):
+                        softmax_scale: float = 0.0, want_lse: bool = True,
+                        qk_mode: int = SQG_QK_EXACT):
     """packed_kv_attention(Q, Kpack, Vpack, scales) -> (O, lse).
 
     `store` is what streamed_qkv_quant returned (or the same keys).  O is [N, d]
-    in the model basis; lse is fp32 [H, N] (natural log)."""
+    in the model basis; lse is fp32 [H, N] (natural log).  qk_mode SQG_QK_FP8 takes
+    the scores on block-scaled fp8 operands (approximation tier)."""
     lib = load()
     q = store["q"] if q is None else q
     if q is None:
         raise ValueError("no Q: the store was built without one, pass q=")
     N, d = q.shape
     a, _keep, o, lse = _attn_args(store, N, d, q.device, q_begin, q_end, kv_begin, kv_end, kv_block,
-                                  accumulate, o, lse, o_dtype, softmax_scale, want_lse)
+                                  accumulate, o, lse, o_dtype, softmax_scale, want_lse, qk_mode)
     a.q, a.ldq = _dev_ptr(q, "q"), q.stride(0)
     _check(lib.sqg_packed_kv_attention(ctypes.byref(a), _stream(q.device)))
     return o, lse
@@ -342,7 +347,8 @@ def packed_kv_attention_qrecompute(store: Dict, x: torch.Tensor, w_qkv: torch.Te
                                    kv_end: int = 0, kv_block: int = 0, accumulate: bool = False,
                                    o: Optional[torch.Tensor] = None,
                                    lse: Optional[torch.Tensor] = None, o_dtype=torch.float32,
-                                   softmax_scale: float = 0.0, want_lse: bool = True):
+                                   softmax_scale: float = 0.0, want_lse: bool = True,
+                                   qk_mode: int = SQG_QK_EXACT):
     """Attention over the packed store with Q recomputed from x chunk by chunk -> (O, lse).
 
     The store may come from streamed_qkv_quant(..., emit=SQG_EMIT_KV): no [N, d] Q
@@ -353,7 +359,7 @@ def packed_kv_attention_qrecompute(store: Dict, x: torch.Tensor, w_qkv: torch.Te
         if t.dtype != torch.bfloat16 or t.stride(-1) != 1:
             raise ValueError("%s must be a row-major bf16 tensor" % nm)
     a, _keep, o, lse = _attn_args(store, N, d, x.device, q_begin, q_end, kv_begin, kv_end, kv_block,
-                                  accumulate, o, lse, o_dtype, softmax_scale, want_lse)
+                                  accumulate, o, lse, o_dtype, softmax_scale, want_lse, qk_mode)
     n_q = (q_end if q_end else N) - q_begin
     if workspace is None:
         need = qrecompute_workspace_bytes(max(n_q, 0), d, q_chunk_rows)
@@ -448,14 +454,14 @@ def packed_kv_attention_staged(staged: Dict, q: torch.Tensor, q_begin: int = 0, 
                                kv_begin: int = 0, kv_end: int = 0, accumulate: bool = False,
                                o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                                o_dtype=torch.float32, softmax_scale: float = 0.0,
-                               want_lse: bool = True):
+                               want_lse: bool = True, qk_mode: int = SQG_QK_EXACT):
     """packed_kv_attention against the host-staged store: blocks are copied in one at a
     time and merged through the LSE.  -> (O, lse)."""
     lib = load()
     N, d = q.shape
     a, _keep, o, lse = _attn_args(staged_view(staged), N, d, q.device, q_begin, q_end, kv_begin,
                                   kv_end, 0, accumulate, o, lse, o_dtype, softmax_scale,
-                                  want_lse or staged["n_blocks"] > 1)
+                                  want_lse or staged["n_blocks"] > 1, qk_mode)
     a.q, a.ldq = _dev_ptr(q, "q"), q.stride(0)
     s = _staged_struct(staged)
     _check(lib.sqg_packed_kv_attention_staged(ctypes.byref(a), ctypes.byref(s), _stream(q.device)))

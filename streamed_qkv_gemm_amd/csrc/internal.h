@@ -68,7 +68,7 @@ struct AttnParams {
   int32_t o_dtype;
   int32_t accumulate;
   float scale_log2;        // softmax scale * log2(e)
-  int32_t pad_;
+  int32_t qk_mode;         // 0: f16 high + remainder query; 1: block-scaled fp8 QK^T
   SegTable seg;
 };
 

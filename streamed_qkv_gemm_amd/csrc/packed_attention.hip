@@ -109,10 +109,30 @@ struct TileRegs {
   uint32_t crow;
 };
 
+// E8M0 exponent of a block whose largest magnitude is a (a finite fp32 >= 0): the
+// smallest e with a <= 448 * 2^e, from the bit pattern (a = 1.m * 2^(ef - 127), and
+// 448 = 1.75 * 2^8), clamped to [-127, 127]; -127 for a zero block.
+__device__ __forceinline__ int e8m0_exponent(float a) {
+  const uint32_t b = __float_as_uint(a);
+  if (a <= 0.0f) return -127;
+  const int e = (int)(b >> 23) - 135 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// fp8 K rows in LDS: 128 codes of one key, dim d at byte swap(bits 3, 4 of d) so that
+// a lane's 16-byte halves of a 64-dim chunk are the dims the scaled MFMA pairs with
+// the query bytes held in registers (see the QK^T step)
+constexpr int kK8Stride = 128 + 16;
+
+template <bool kFp8QK>
 __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(16))) _Float16 sK[2][kKTile];
   __shared__ __attribute__((aligned(16))) _Float16 sV[2][kVTile];
-  __shared__ __attribute__((aligned(16))) _Float16 sQl[kWaves][32 * kHeadDim];
+  __shared__ __attribute__((aligned(16))) _Float16 sQl[kFp8QK ? 1 : kWaves][32 * kHeadDim];
+  __shared__ uint32_t sKe[2][kBKV];   // fp8 QK: the four E8M0 exponents of each key (byte g)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -122,62 +142,147 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
   const int head = blockIdx.y;
   const int64_t N = p.n_tokens;
 
-  // ---- query tile: rotate once, keep as f16 MFMA B operands (high part + remainder)
+  // ---- query tile: rotate once, keep as MFMA B operands: f16 high part + remainder,
+  // or (fp8 QK) E4M3 codes with one E8M0 exponent per group of 32 dims
   const int64_t qrow = p.q_begin + (int64_t)blockIdx.x * kBQ + 32 * wave + l32;
   const bool qvalid = qrow < p.q_end;
   f16x8 qf[8], ql[8];
+  i32x8 q8[2];
+  uint32_t q8e[2];
   {
     const uint16_t* src = p.q + ((qvalid ? qrow : p.q_begin) - p.q_row0) * p.ldq + head * kHeadDim + 8 * hsel;
-    // element e(ks, j) = 16 ks + 8 hsel + j: bits 0-2 = j, bit 3 = lane pair, bits 4-6 = ks
+    // element e(ks, j) = 16 ks + 8 hsel + j: bits 0-2 = j, bit 3 = lane pair, bits 4-6 = ks.
+    // The fp8 tier quantises the rotated query, so there the transform runs in fp64:
+    // the sum of 128 bf16 values is then exact and one fp64 product rounded to fp32
+    // gives the correctly rounded rotated value, on which the quantiser decides.
     float v[8][8];
+    if constexpr (kFp8QK) {
+      double w[8][8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (qvalid) raw = *reinterpret_cast<const u32x4*>(src + 16 * ks);
+      for (int ks = 0; ks < 8; ++ks) {
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (qvalid) raw = *reinterpret_cast<const u32x4*>(src + 16 * ks);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[ks][2 * j] = bf16_lo(raw[j]);
-        v[ks][2 * j + 1] = bf16_hi(raw[j]);
+        for (int j = 0; j < 4; ++j) {
+          w[ks][2 * j] = (double)bf16_lo(raw[j]);
+          w[ks][2 * j + 1] = (double)bf16_hi(raw[j]);
+        }
       }
-    }
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int bit = 1; bit < 8; bit <<= 1)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            if (j & bit) continue;
+            const double x = w[ks][j], y = w[ks][j | bit];
+            w[ks][j] = x + y;
+            w[ks][j | bit] = x - y;
+          }
 #pragma unroll
       for (int bit = 1; bit < 8; bit <<= 1)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (j & bit) continue;
-          const float x = v[ks][j], y = v[ks][j | bit];
-          v[ks][j] = x + y;
-          v[ks][j | bit] = x - y;
+        for (int ks = 0; ks < 8; ++ks) {
+          if (ks & bit) continue;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const double x = w[ks][j], y = w[ks | bit][j];
+            w[ks][j] = x + y;
+            w[ks | bit][j] = x - y;
+          }
         }
 #pragma unroll
-    for (int bit = 1; bit < 8; bit <<= 1)
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint64_t b = __builtin_bit_cast(uint64_t, w[ks][j]);
+          const uint64_t pb = (uint64_t)xor32u((uint32_t)b) | ((uint64_t)xor32u((uint32_t)(b >> 32)) << 32);
+          const double pr = __builtin_bit_cast(double, pb);
+          v[ks][j] = (float)((hsel ? (pr - w[ks][j]) : (w[ks][j] + pr)) * 0.08838834764831845);
+        }
+    } else {
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        if (ks & bit) continue;
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (qvalid) raw = *reinterpret_cast<const u32x4*>(src + 16 * ks);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float x = v[ks][j], y = v[ks | bit][j];
-          v[ks][j] = x + y;
-          v[ks | bit][j] = x - y;
+        for (int j = 0; j < 4; ++j) {
+          v[ks][2 * j] = bf16_lo(raw[j]);
+          v[ks][2 * j + 1] = bf16_hi(raw[j]);
         }
       }
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+      for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float pr = xor32(v[ks][j]);
-        const float r = (hsel ? (pr - v[ks][j]) : (v[ks][j] + pr)) * kInvSqrtHeadDim;
-        const _Float16 hi = (_Float16)r;
-        qf[ks][j] = hi;
-        ql[ks][j] = (_Float16)(r - (float)hi);
+        for (int bit = 1; bit < 8; bit <<= 1)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            if (j & bit) continue;
+            const float x = v[ks][j], y = v[ks][j | bit];
+            v[ks][j] = x + y;
+            v[ks][j | bit] = x - y;
+          }
+#pragma unroll
+      for (int bit = 1; bit < 8; bit <<= 1)
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          if (ks & bit) continue;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float x = v[ks][j], y = v[ks | bit][j];
+            v[ks][j] = x + y;
+            v[ks | bit][j] = x - y;
+          }
+        }
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float pr = xor32(v[ks][j]);
+          v[ks][j] = (hsel ? (pr - v[ks][j]) : (v[ks][j] + pr)) * kInvSqrtHeadDim;
+        }
+    }
+    if constexpr (!kFp8QK) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const _Float16 hi = (_Float16)v[ks][j];
+          qf[ks][j] = hi;
+          ql[ks][j] = (_Float16)(v[ks][j] - (float)hi);
+        }
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        *reinterpret_cast<f16x8*>(&sQl[wave][(ks * 64 + lane) * 8]) = ql[ks];
+    } else {
+      // group g = dims 32 g .. + 31 = k-steps 2 g, 2 g + 1 of both lanes of the pair
+      int eg[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float a = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a = fmaxf(a, fmaxf(fabsf(v[2 * g][j]), fabsf(v[2 * g + 1][j])));
+        eg[g] = e8m0_exponent(fmaxf(a, xor32(a)));
       }
+      // B operand of chunk c (dims 64 c .. + 63): byte b = element (k-step 4 c + b / 8, b % 8)
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      *reinterpret_cast<f16x8*>(&sQl[wave][(ks * 64 + lane) * 8]) = ql[ks];
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int ks = 4 * c + kk;
+          const int e = eg[ks >> 1];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[ks][4 * h], -e), ldexpf(v[ks][4 * h + 1], -e), 0, false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[ks][4 * h + 2], -e), ldexpf(v[ks][4 * h + 3], -e), w, true);
+            q8[c][2 * kk + h] = w;
+          }
+        }
+        q8e[c] = (uint32_t)(eg[2 * c + hsel] + 127);   // this lane supplies block hsel's exponent
+      }
+    }
   }
-  const _Float16* qlw = sQl[wave];
+  const _Float16* qlw = sQl[kFp8QK ? 0 : wave];
 
   // ---- per-thread maps for the K/V tile loads (64 keys per tile, 512 threads): waves
   // 0-3 bring K, waves 4-7 bring V; thread (key, grp) moves group grp (32 values) of one
@@ -259,10 +364,35 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
         for (int w = 0; w < 4; ++w) o[4 * i + w] = bf16x2_to_f16x2(b[w]);
       }
     }
+    if (kFp8QK && !vside) {
+      // K as E4M3 codes of value / 2^e with e the group's E8M0 exponent; bytes of dims
+      // 8..15 and 16..23 of the group trade places (the swap of dim bits 3 and 4)
+      f16x2 m2 = {(_Float16)0.0f, (_Float16)0.0f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4 v = {o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
-      *reinterpret_cast<u32x4*>(dst + 8 * i) = v;
+      for (int i = 0; i < 16; ++i) m2 = __builtin_elementwise_max(m2, __builtin_elementwise_abs(__builtin_bit_cast(f16x2, o[i])));
+      const float a = fmaxf((float)m2[0], (float)m2[1]);
+      const int e = e8m0_exponent(a);
+      const float sc = a > 0.0f ? ldexpf(1.0f, e) : 1.0f;
+      uint32_t w[8];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const s16x2 zero = {0, 0};
+        s16x2 r2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(zero, __builtin_bit_cast(f16x2, o[2 * d]), sc, false);
+        r2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r2, __builtin_bit_cast(f16x2, o[2 * d + 1]), sc, true);
+        w[d] = __builtin_bit_cast(uint32_t, r2);
+      }
+      uint8_t* k8 = reinterpret_cast<uint8_t*>(sK[stage]) + tkey * kK8Stride + 32 * tgrp;
+      const u32x4 lo = {w[0], w[1], w[4], w[5]};
+      const u32x4 hi = {w[2], w[3], w[6], w[7]};
+      *reinterpret_cast<u32x4*>(k8) = lo;
+      *reinterpret_cast<u32x4*>(k8 + 16) = hi;
+      reinterpret_cast<uint8_t*>(sKe[stage])[4 * tkey + tgrp] = (uint8_t)(e + 127);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 v = {o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+        *reinterpret_cast<u32x4*>(dst + 8 * i) = v;
+      }
     }
   };
 
@@ -316,6 +446,28 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks & 1][kb], lo[ks & 1], s[kb], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // fp8 QK^T: per 32-key block and 64-dim chunk one block-scaled MFMA.  A lane's
+  // operand bytes are k slots 16 hsel + b % 16 + 32 (b / 16); slot k carries dim k with
+  // bits 3 and 4 swapped on both sides (the query bytes by construction, the key bytes
+  // by their LDS order), so the MFMA's 32-slot scale blocks are exactly the groups.
+  auto do_qk8 = [&](int stage, f32x16 (&s)[kKB]) {
+    const uint8_t* K8 = reinterpret_cast<const uint8_t*>(sK[stage]);
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) {
+      const uint32_t ew = sKe[stage][32 * kb + l32];
+      const uint8_t* row = K8 + (32 * kb + l32) * kK8Stride + 16 * hsel;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(row + 64 * c);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(row + 64 * c + 32);
+        const i32x8 A = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+        const int ea = (int)((ew >> (8 * (2 * c + hsel))) & 0xffu);
+        const f32x16 acc = c == 0 ? f32x16{} : s[kb];
+        s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, q8[c], acc, 0, 0, 0, ea, 0, (int)q8e[c]);
+      }
     }
   };
 
@@ -401,7 +553,10 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
     if (!lead) do_dq(it);
     f32x16 s[kKB];
     f16x8 pf[2 * kKB];
-    do_qk(stage, s);
+    if constexpr (kFp8QK)
+      do_qk8(stage, s);
+    else
+      do_qk(stage, s);
     do_softmax(key0, s, pf);
     do_pv(stage, pf);
     if (lead) do_dq(it);
@@ -478,8 +633,12 @@ int launch_packed_attention(const AttnParams& p, void* stream) {
   const int64_t nq = p.q_end - p.q_begin;
   if (nq <= 0 || p.kv_end <= p.kv_begin) return 0;
   const int64_t tiles = (nq + kBQ - 1) / kBQ;
-  hipLaunchKernelGGL(packed_attention_kernel, dim3((unsigned)tiles, (unsigned)p.n_heads),
-                     dim3(kThreads), 0, (hipStream_t)stream, p);
+  if (p.qk_mode == 1)
+    hipLaunchKernelGGL(packed_attention_kernel<true>, dim3((unsigned)tiles, (unsigned)p.n_heads),
+                       dim3(kThreads), 0, (hipStream_t)stream, p);
+  else
+    hipLaunchKernelGGL(packed_attention_kernel<false>, dim3((unsigned)tiles, (unsigned)p.n_heads),
+                       dim3(kThreads), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
 

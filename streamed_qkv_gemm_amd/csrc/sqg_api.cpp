@@ -246,6 +246,9 @@ int attn_prepare(const sqg_attn_args* a, bool check_q, sqg::AttnParams* p, int64
                 "accumulate and kv_block > 0 need an lse buffer and o_dtype SQG_F32");
   if (!(std::isfinite(a->softmax_scale) && a->softmax_scale >= 0.0f))
     return fail(SQG_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+  if (a->qk_mode != SQG_QK_EXACT && a->qk_mode != SQG_QK_FP8)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "unknown qk_mode %d", a->qk_mode);
+  if (a->reserved != 0) return fail(SQG_ERR_INVALID_ARGUMENT, "attention reserved field not 0");
   if (N == 0 || q_end == a->q_begin) {
     *empty = true;
     return SQG_OK;
@@ -284,6 +287,7 @@ int attn_prepare(const sqg_attn_args* a, bool check_q, sqg::AttnParams* p, int64
   p->d_model = a->d_model;
   p->n_heads = a->n_heads;
   p->o_dtype = a->o_dtype;
+  p->qk_mode = a->qk_mode;
   const double scale = a->softmax_scale > 0.0f ? (double)a->softmax_scale : 1.0 / std::sqrt(128.0);
   p->scale_log2 = (float)(scale * 1.4426950408889634);
   p->seg = seg_table(L);

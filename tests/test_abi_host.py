@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 10
     for n in names:
         assert hasattr(lib, n), n
-    assert sqg.version() == 120
+    assert sqg.version() == 130
 
 
 def test_struct_sizes_match_binding():
@@ -280,6 +280,8 @@ def test_zero_tokens_is_a_noop():
     (dict(o=FAKE + 4), -3),
     (dict(ldo=500), -1),
     (dict(kpack=None), -1),
+    (dict(qk_mode=2), -1),
+    (dict(reserved=1), -1),
 ])
 def test_attention_argument_errors(kw, status):
     lib = sqg.load()

@@ -1,0 +1,112 @@
+"""GPU parity of the low-precision QK^T tier (SQG_QK_FP8): scores on block-scaled fp8
+operands ([VL] kvi8s section: an approximation tier with rotated Q and K and QK^T on
+low-precision matrix cores).  The oracle quantises the same operands the same way
+(`oracle.attention_fp8qk_rotated`), so the kernel is held to the G3 gate against it;
+against the exact tier the error is only reported and bounded."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle import BF16, INT4, INT8
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def build(lib, N, d, ranges, seed, norm_rope=False):
+    x = synth.make_x(N, d, 0.01, seed=seed, device=DEV)
+    w = synth.make_w(d, seed=seed + 1, device=DEV)
+    kw = {}
+    if norm_rope:
+        qn, kn = synth.make_norm_weights(seed + 2)
+        kw = dict(q_norm_w=qn.to(DEV), k_norm_w=kn.to(DEV))
+        kw["rope_cos"], kw["rope_sin"] = lib.rope_table(N, 10000.0, device=DEV)
+    store = lib.streamed_qkv_quant(x, w, ranges=ranges, **kw)
+    torch.cuda.synchronize()
+    H = d // 128
+    layout, _ = oracle.packed_layout(N, H, oracle.range_segments(N, ranges, n_heads=H))
+    return x, w, kw, store, layout
+
+
+def oracle_rows(store, layout, rows, N, H, **kw):
+    qb = synth.bf16_bits(store["q"])[rows]
+    return oracle.attention_rows_from_store(qb, rows, host(store["kpack"]), host(store["vpack"]),
+                                            host(store["kscale"]), host(store["vscale"]), layout,
+                                            H, N, **kw)
+
+
+def gate(got, want, lse, lse_want):
+    err = np.abs(got - want)
+    rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+    dl = np.abs(lse - lse_want)
+    where = np.argwhere(dl > 2e-3)
+    msg = "max-abs %.3g rel %.3g lse %.3g; %d (head, row) over 2e-3: %s" % (
+        err.max(), rel, dl.max(), len(where), where[:10].tolist())
+    print(msg)
+    assert err.max() <= 2e-2, msg
+    assert rel <= 5e-3, msg
+    assert dl.max() <= 2e-3, msg
+    return err.max(), rel
+
+
+CASES = [
+    (1024, 512, None, False),
+    (1000, 512, [(0, 128, INT8), (128, 1000, INT4)], True),
+    (777, 768, [(0, 256, BF16), (256, 640, INT4, 0b101), (640, 777, INT8)], True),
+]
+
+
+@pytest.mark.parametrize("N,d,ranges,nr", CASES)
+def test_fp8qk_matches_the_fp8_oracle(lib, N, d, ranges, nr):
+    x, w, kw, store, layout = build(lib, N, d, ranges, 701, nr)
+    H = d // 128
+    o, lse = lib.packed_kv_attention(store, qk_mode=lib.SQG_QK_FP8)
+    o_ex, _ = lib.packed_kv_attention(store)
+    torch.cuda.synchronize()
+    rows = np.arange(0, N, 3)
+    want, lse_want = oracle_rows(store, layout, rows, N, H, qk="fp8")
+    gate(host(o)[rows].astype(np.float64), want, host(lse)[:, rows], lse_want)
+    # the approximation itself: against the exact tier's oracle it moves, but boundedly
+    exact, _ = oracle_rows(store, layout, rows, N, H)
+    rel_exact = np.linalg.norm(host(o)[rows] - exact) / np.linalg.norm(exact)
+    assert 1e-4 < rel_exact < 0.1, rel_exact
+    assert not torch.equal(o, o_ex)
+
+
+def test_fp8qk_kv_blocks_and_accumulate(lib):
+    N, d = 1000, 512
+    x, w, kw, store, layout = build(lib, N, d, [(0, 256, INT8), (256, N, INT4)], 711)
+    H = d // 128
+    o_b, l_b = lib.packed_kv_attention(store, kv_block=256, qk_mode=lib.SQG_QK_FP8)
+    o, l = lib.packed_kv_attention(store, kv_end=512, qk_mode=lib.SQG_QK_FP8)
+    lib.packed_kv_attention(store, kv_begin=512, accumulate=True, o=o, lse=l, qk_mode=lib.SQG_QK_FP8)
+    torch.cuda.synchronize()
+    rows = np.arange(0, N, 7)
+    want, lse_want = oracle_rows(store, layout, rows, N, H, qk="fp8", kv_block=256)
+    gate(host(o_b)[rows].astype(np.float64), want, host(l_b)[:, rows], lse_want)
+    want2, lse2 = oracle_rows(store, layout, rows, N, H, qk="fp8")
+    gate(host(o)[rows].astype(np.float64), want2, host(l)[:, rows], lse2)
+
+
+def test_fp8qk_through_qrecompute_and_staging(lib):
+    N, d = 1100, 512
+    ranges = [(0, 128, INT8), (128, N, INT4)]
+    x, w, kw, store, layout = build(lib, N, d, ranges, 721, True)
+    q_kw = {k: v for k, v in kw.items() if k != "k_norm_w"}
+    ref, lref = lib.packed_kv_attention(store, kv_block=512, qk_mode=lib.SQG_QK_FP8)
+    kv = lib.streamed_qkv_quant(x, w, ranges=ranges, emit=lib.SQG_EMIT_KV, **kw)
+    o1, l1 = lib.packed_kv_attention_qrecompute(kv, x, w, q_chunk_rows=384, kv_block=512,
+                                                qk_mode=lib.SQG_QK_FP8, **q_kw)
+    st = lib.alloc_staged(N, d, 512, ranges, device=DEV)
+    lib.streamed_qkv_quant_staged(x, w, st, emit=lib.SQG_EMIT_KV, **kw)
+    o2, l2 = lib.packed_kv_attention_staged(st, store["q"], qk_mode=lib.SQG_QK_FP8)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, ref) and torch.equal(l1, lref)
+    assert torch.equal(o2, ref) and torch.equal(l2, lref)
