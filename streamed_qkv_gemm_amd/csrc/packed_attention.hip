@@ -47,7 +47,12 @@ constexpr int kBKV = 64;              // keys per tile
 constexpr int kKB = kBKV / 32;        // 32-key MFMA blocks per tile
 constexpr int kKStride = 128 + 8;     // f16 per K row in LDS (272 B)
 constexpr int kKTile = kBKV * kKStride;
-constexpr int kVTile = kBKV * kKStride;  // V row-major like K
+// V rows: 160 f16 per key (80 dwords: consecutive keys start 16 banks apart), and dim
+// bits 3-4 XORed with bits 2-3 of the key, so that the decode's 16-byte row writes and
+// the transposing 8-byte reads (8 keys x 16 dims per instruction) spread over all banks.
+constexpr int kVStride = kHeadDim + 32;
+constexpr int kVTile = kBKV * kVStride;
+__device__ __forceinline__ int vcol(int k, int d) { return d ^ (((k >> 2) & 3) << 3); }
 constexpr float kRescaleLog2 = 8.0f;  // move the running max only past this growth
 
 
@@ -387,6 +392,13 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
       *reinterpret_cast<u32x4*>(k8) = lo;
       *reinterpret_cast<u32x4*>(k8 + 16) = hi;
       reinterpret_cast<uint8_t*>(sKe[stage])[4 * tkey + tgrp] = (uint8_t)(e + 127);
+    } else if (vside) {
+      _Float16* vrow = sV[stage] + tkey * kVStride;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 v = {o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+        *reinterpret_cast<u32x4*>(vrow + vcol(tkey, 32 * tgrp + 8 * i)) = v;
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -520,13 +532,17 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
     // 16 ks + 4 hsel + 0..3 and 16 ks + 8 + 4 hsel + 0..3 (the MFMA's k slots 8 hsel + e
     // with bits 2 and 3 swapped, matching the key order of the P operand).  Each 16-lane
     // group reads 4 keys x 16 dims: lane c points at key (c / 4), dims 4 (c % 4) .. + 3.
-    const _Float16* vbase = V + (4 * hsel + ((lane & 15) >> 2)) * kKStride + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // key k = 16 ks + 8 half + vk (vk = 4 hsel + (lane % 16) / 4), so bits 2-3 of k are
+    // (2 half + hsel) % 4 for every ks: one base per half, ks and db as offsets
+    const int vk = 4 * hsel + ((lane & 15) >> 2);
+    const int vd = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const _Float16* vb0 = V + vk * kVStride + vcol(vk, vd);
+    const _Float16* vb1 = V + (vk + 8) * kVStride + vcol(vk + 8, vd);
     auto rd = [&](int ks, int b) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const _Float16* a = vbase + 16 * ks * kKStride + 32 * db;
-        const f16x4 lo = tr_read_f16x4(a);
-        const f16x4 hi = tr_read_f16x4(a + 8 * kKStride);
+        const f16x4 lo = tr_read_f16x4(vb0 + 16 * ks * kVStride + 32 * db);
+        const f16x4 hi = tr_read_f16x4(vb1 + 16 * ks * kVStride + 32 * db);
         vf[b][db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
     };
