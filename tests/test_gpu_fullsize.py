@@ -77,3 +77,52 @@ def test_fullsize_parity(lib, name):
         rel = np.linalg.norm(og[:, sl] - o_ref[:, sl]) / np.linalg.norm(o_ref[:, sl])
         assert err.max() <= 2e-2 and rel <= 5e-3, (name, h, err.max(), rel)
         assert np.max(np.abs(lg[h] - lse_ref[h])) <= 2e-3
+
+
+def test_fullsize_variants_217k(lib):
+    """The bench's extra measurements at 217,088 tokens x 56 heads, in its launch
+    configuration: the fp8 QK^T tier against the fp8 oracle on sampled rows, and the
+    Q-recompute and host-staged variants equal to the device path on sampled rows."""
+    wl = synth.WORKLOADS["h3_217k_normrope"]
+    N, d, H = wl.n_tokens, wl.d_model, wl.n_heads
+    print("[fullsize] variants N=%d d=%d" % (N, d), flush=True)
+    x, w, norm = build_inputs(wl)
+    kw = dict(q_norm_w=norm[0].to(DEV), k_norm_w=norm[1].to(DEV))
+    kw["rope_cos"], kw["rope_sin"] = lib.rope_table(N, 10000.0, device=DEV)
+    store = lib.streamed_qkv_quant(x, w, ranges=wl.ranges, chunk_rows=wl.chunk_rows, **kw)
+    o, lse = lib.packed_kv_attention(store, kv_block=wl.kv_block)
+    o8, l8 = lib.packed_kv_attention(store, kv_block=wl.kv_block, qk_mode=lib.SQG_QK_FP8)
+    torch.cuda.synchronize()
+    qrows = synth.sample_rows(N, 8, seed=wl.seed_base + 7, must=[0, N - 1]).numpy()
+    heads = [1, H - 2]
+    qb = synth.bf16_bits(store["q"])
+    layout, _ = oracle.packed_layout(N, H, oracle.range_segments(N, wl.ranges))
+    args = (host(store["kpack"]), host(store["vpack"]), host(store["kscale"]), host(store["vscale"]),
+            layout, H, N)
+    want, lse_want = oracle.attention_rows_from_store(qb[qrows], qrows, *args, kv_block=wl.kv_block,
+                                                      heads=heads, qk="fp8")
+    og, lg = host(o8)[qrows], host(l8)[:, qrows]
+    for h in heads:
+        sl = slice(128 * h, 128 * h + 128)
+        err = np.abs(og[:, sl] - want[:, sl])
+        rel = np.linalg.norm(og[:, sl] - want[:, sl]) / np.linalg.norm(want[:, sl])
+        assert err.max() <= 2e-2 and rel <= 5e-3, ("fp8", h, err.max(), rel)
+        assert np.max(np.abs(lg[h] - lse_want[h])) <= 2e-3
+    qr = torch.from_numpy(qrows).to(DEV)
+    o_ref, l_ref = o[qr].clone(), lse[:, qr].clone()
+    del o8, l8, o, lse
+    torch.cuda.empty_cache()
+    # Q-recompute from a K/V-only store
+    kv = lib.streamed_qkv_quant(x, w, ranges=wl.ranges, chunk_rows=wl.chunk_rows, emit=lib.SQG_EMIT_KV, **kw)
+    q_kw = {k: v for k, v in kw.items() if k != "k_norm_w"}
+    o1, l1 = lib.packed_kv_attention_qrecompute(kv, x, w, kv_block=wl.kv_block, **q_kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[qr], o_ref) and torch.equal(l1[:, qr], l_ref)
+    del o1, l1, kv
+    torch.cuda.empty_cache()
+    # host-staged K/V in blocks of the KV-block size
+    st = lib.alloc_staged(N, d, wl.kv_block, wl.ranges, device=DEV)
+    lib.streamed_qkv_quant_staged(x, w, st, emit=lib.SQG_EMIT_KV, **kw)
+    o2, l2 = lib.packed_kv_attention_staged(st, store["q"])
+    torch.cuda.synchronize()
+    assert torch.equal(o2[qr], o_ref) and torch.equal(l2[:, qr], l_ref)
