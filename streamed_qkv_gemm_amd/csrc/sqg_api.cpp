@@ -766,4 +766,16 @@ SQG_API int sqg_test_fwht_f32(const float* in, float* out, int64_t rows, int32_t
   return st == SQG_OK ? ok() : st;
 }
 
+SQG_API int sqg_test_mfma_rate(int32_t dtype, int64_t iters, int64_t n_blocks, float* sink,
+                               void* stream) {
+  if (dtype != 0 && dtype != 1) return fail(SQG_ERR_INVALID_ARGUMENT, "dtype must be 0 (f16) or 1 (bf16)");
+  if (iters <= 0 || n_blocks <= 0 || n_blocks > 0x7fffffff)
+    return fail(SQG_ERR_INVALID_ARGUMENT, "iters and n_blocks must be positive (n_blocks < 2^31)");
+  if (!sink) return fail(SQG_ERR_INVALID_ARGUMENT, "sink is NULL");
+  if (!aligned16(sink)) return fail(SQG_ERR_MISALIGNED, "sink must be 16-byte aligned");
+  const int st = launch_status(sqg::launch_test_mfma_rate(dtype, iters, n_blocks, sink, stream),
+                               "test_mfma_rate launch");
+  return st == SQG_OK ? ok() : st;
+}
+
 }  // extern "C"

@@ -296,6 +296,11 @@ def test_test_entry_argument_errors():
     assert lib.sqg_test_quant_pack_f32(FAKE + 4, 10, 0, FAKE, FAKE, None) == -3
     assert lib.sqg_test_quant_pack_f32(FAKE, 0, 0, None, None, None) == 0
     assert lib.sqg_test_fwht_f32(FAKE, FAKE, -1, 0, None) == -1
+    assert lib.sqg_test_mfma_rate(2, 10, 1, FAKE, None) == -1
+    assert lib.sqg_test_mfma_rate(0, 0, 1, FAKE, None) == -1
+    assert lib.sqg_test_mfma_rate(0, 10, 0, FAKE, None) == -1
+    assert lib.sqg_test_mfma_rate(0, 10, 1, None, None) == -1
+    assert lib.sqg_test_mfma_rate(1, 10, 1, FAKE + 4, None) == -3
 
 
 def test_binding_refuses_cpu_tensors():

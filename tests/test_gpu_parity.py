@@ -160,6 +160,14 @@ def test_fwht_random_inputs_close(lib):
     assert np.max(np.abs(out - ref)) <= 8 * 2 ** -24 * np.max(np.abs(u)) * math.sqrt(128)
 
 
+def test_mfma_rate_measurement_is_plausible(lib):
+    # the matrix-core-only kernel behind the bench's sustained-rate figure: positive and
+    # below the published dense peak (2.5 PFLOP/s for f16 and bf16)
+    for dtype in (0, 1):
+        r = lib.test_mfma_rate(dtype, iters=2000, repeats=2)
+        assert 50.0 < r < 2600.0, (dtype, r)
+
+
 # ----------------------------------------------------------------------------- projection exactness
 def test_integer_projection_bit_exact_and_chunk_invariant(lib):
     # integer-valued x, W in [-4, 4] at d = 512: all fp32 sums are exact, so Q and,
