@@ -13,13 +13,19 @@
 // store; kvi8r section: rotated store.)
 //
 // Workgroup tile: 256 output columns (2 heads) x 256 tokens, K-step 64, four
-// waves in a 2 x 2 grid, each wave owning one head x 128 tokens.  Slices of x and
-// W are fetched with range-checked buffer loads two K-steps ahead of their LDS
-// store (two register sets), LDS is double-buffered, and scheduling groups thread
-// the next step's operand reads between each step's MFMAs.  The transposed
+// waves in a 2 x 2 grid, each wave owning one head x 128 tokens.  The x and W
+// slices of a K-step go from HBM straight into LDS (range-checked buffer loads with
+// the LDS bit, no register staging), into two stages; W stays k-major there and
+// its MFMA operand comes out through transposing LDS reads.  One barrier per
+// K-step sits before the step's last k-substep, whose 16 MFMAs then run beside the
+// loads of the slices two steps ahead and the next step's first operand reads;
+// scheduling groups thread each substep's operand reads between the MFMAs of the
+// substep before.  The transposed
 // product puts one token per lane column of each 32x32 MFMA block, so the head's
 // 128 values of a token sit in one lane pair: the Hadamard, the RMSNorm sum and the
 // group absmax each need a single exchange with lane ^ 32 (device_common.h).
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -29,13 +35,9 @@ namespace {
 constexpr int kBM = 256;        // output columns per workgroup
 constexpr int kBN = 256;        // tokens per workgroup
 constexpr int kBK = 64;         // reduction slice per stage
-constexpr int kStride = kBK + 8;  // bf16 per LDS row (144 B: conflict-free 16-byte reads)
-constexpr int kTileElems = 256 * kStride;
+constexpr int kXBytes = kBN * kBK * 2;          // x slice [256 tokens][64 k]: 32 KiB
+constexpr int kStageBytes = kXBytes + kBK * kBM * 2;  // + W slice [64 k][256 cols]
 constexpr int kGroupRows = 32;  // token tiles per raster group (L2 reuse of W and x)
-
-__device__ __forceinline__ uint32_t perm_b32(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi_src, lo_src, sel);
-}
 
 // RMSNorm of one head vector in column layout: u * w / sqrt(mean(u^2) + eps)
 __device__ __forceinline__ void rms_norm_cols(float (&u)[4][16], const float* __restrict__ w,
@@ -79,7 +81,10 @@ __device__ __forceinline__ void rope_cols(float (&u)[4][16], const float* __rest
 }
 
 __global__ __launch_bounds__(256, 1) void qkv_quant_kernel(const QkvParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kTileElems];  // [stage][A=W^T, B=x]
+  // two stages as two arrays, so that the compiler sees that a stage being filled and
+  // the stage being read never alias (no wait on the fills before the reads)
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -103,53 +108,44 @@ __global__ __launch_bounds__(256, 1) void qkv_quant_kernel(const QkvParams p) {
   const int col0 = col_tile * kBM;
   const int64_t tok0 = p.row_begin + (int64_t)tok_tile * kBN;
 
-  // ---- global -> register staging maps
-  // x tile [256 tokens][64 k]: thread loads 16 B chunk (tid & 7) of rows (tid >> 3) + 32 i
-  const int xc = tid & 7;
-  const int xr = tid >> 3;
-  // W tile [64 k][256 cols]: thread loads an 8 k x 8 col block: k rows 8 (tid & 7) + i,
-  // cols 8 (tid >> 3) .. + 7, and writes it transposed (k contiguous per column)
-  const int wk = tid & 7;
-  const int wcb = tid >> 3;
-
-  // x rows past the end of the sequence read as zero through the buffer's size
+  // ---- operand slices go from HBM straight into LDS (buffer loads with the LDS bit:
+  // lane L of a wave's load writes bytes [16 L, 16 L + 16) of a 1 KiB LDS block), two
+  // stages of 64 KiB, each holding the x slice [256 tokens][64 k] (128-byte rows) and
+  // the W slice [64 k][256 cols] (512-byte rows).  Each 16-byte chunk is placed at an
+  // XOR-swizzled slot of its row (the lane loads the chunk that belongs in its slot), so
+  // the MFMA operand reads below hit distinct LDS banks:
+  //   x row t, chunk c (k 8c .. 8c + 7)     at slot c ^ ((t >> 1) & 7)
+  //   W row k, chunk c (cols 8c .. 8c + 7)  at slot c ^ (4 (k & 3))
   const int64_t rows_valid = min((int64_t)kBN, p.n_tokens - tok0);
   const __amdgpu_buffer_rsrc_t xr_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.x + tok0 * p.ldx), 0, (int32_t)(rows_valid * p.ldx * 2), kBufferWord3);
   const __amdgpu_buffer_rsrc_t wr_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.w + col0), 0, (int32_t)0x7fffffff, kBufferWord3);
-  const uint32_t x_off = (uint32_t)((xr * p.ldx + 8 * xc) * 2);
-  const uint32_t x_rowstep = (uint32_t)(32 * p.ldx * 2);
-  const uint32_t w_off = (uint32_t)(((8 * wk) * p.ldw + 8 * wcb) * 2);
-  const uint32_t w_rowstep = (uint32_t)(p.ldw * 2);
-
-  u32x4 xregs[2][8], wregs[2][8];
-  auto load_tiles = [&](int kt, u32x4 (&xreg)[8], u32x4 (&wreg)[8]) {
-    const int32_t kx = kt * kBK * 2;                       // byte offset along k in x rows
-    const int32_t kw = (int32_t)((int64_t)kt * kBK * p.ldw * 2);  // byte offset of k rows in W
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  // wave wv moves x rows 64 wv .. + 63 and W rows 16 wv .. + 15: eight 1 KiB loads each
+  uint32_t xoff[8], woff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int xrow = 64 * wv + 8 * i + (lane >> 3);
+    const int xc = (lane & 7) ^ ((xrow >> 1) & 7);
+    xoff[i] = (uint32_t)(xrow * p.ldx * 2 + 16 * xc);
+    const int wrow = 16 * wv + 2 * i + (lane >> 5);
+    const int wch = (lane & 31) ^ (4 * (wrow & 3));
+    woff[i] = (uint32_t)(wrow * p.ldw * 2 + 16 * wch);
+  }
+  auto issue_loads = [&](int kt, int stage) {
+    uint8_t* xs = (stage ? lds1 : lds0) + wv * 8192;
+    uint8_t* ws = xs + kXBytes;
+    const uint32_t kx = (uint32_t)(kt * kBK * 2);
+    const uint32_t kw = (uint32_t)((int64_t)kt * kBK * p.ldw * 2);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      xreg[i] = __builtin_amdgcn_raw_buffer_load_b128(xr_rsrc, x_off + i * x_rowstep, kx, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr_rsrc, (__attribute__((address_space(3))) void*)(xs + 1024 * i),
+                                               16, xoff[i], kx, 0, 0);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      wreg[i] = __builtin_amdgcn_raw_buffer_load_b128(wr_rsrc, w_off + i * w_rowstep, kw, 0);
-  };
-  auto store_tiles = [&](int stage, const u32x4 (&xreg)[8], const u32x4 (&wreg)[8]) {
-    uint16_t* sA = lds[stage][0];
-    uint16_t* sB = lds[stage][1];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4*>(sB + (xr + 32 * i) * kStride + 8 * xc) = xreg[i];
-    // 8x8 transpose of bf16: column c gets (k=2j, k=2j+1) pairs from rows 2j, 2j+1
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int m = c >> 1;
-      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-      u32x4 o;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = perm_b32(wreg[2 * j + 1][m], wreg[2 * j][m], sel);
-      *reinterpret_cast<u32x4*>(sA + (8 * wcb + c) * kStride + 8 * wk) = o;
-    }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr_rsrc, (__attribute__((address_space(3))) void*)(ws + 1024 * i),
+                                               16, woff[i], kw, 0, 0);
   };
 
   // ---- main loop
@@ -163,63 +159,102 @@ __global__ __launch_bounds__(256, 1) void qkv_quant_kernel(const QkvParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
 
-  const int nk = p.d_model / kBK;   // a multiple of 4 (d is a multiple of 256)
-  load_tiles(0, xregs[0], wregs[0]);
-  load_tiles(1, xregs[1], wregs[1]);
-  store_tiles(0, xregs[0], wregs[0]);
-  load_tiles(2, xregs[0], wregs[0]);
-  __syncthreads();
-  const int a_row = (128 * wc + l32) * kStride + 8 * hsel;
-  const int b_row = (128 * wt + l32) * kStride + 8 * hsel;
-  // slices are loaded two iterations before they are written to LDS: at the end of
-  // iteration kt the registers holding slice kt + 1 are stored, then reloaded with
-  // slice kt + 3 (clamped to the last slice near the end)
-  auto iteration = [&](int kt, u32x4 (&xreg)[8], u32x4 (&wreg)[8]) {
-    const int stage = kt & 1;
-    const uint16_t* sA = lds[stage][0];
-    const uint16_t* sB = lds[stage][1];
-    bf16x8 af[2][4], bfr[2][4];
+  // A operand (W^T: 32 cols x 16 k per MFMA) by transposing reads: within a 16-lane
+  // group, lane g4 + 4 j points at 4 columns 4 (lane % 4) .. of W row k0 + j and lane i
+  // receives column i of rows k0 .. k0 + 3; two reads (k0, k0 + 4) give the 8 k values
+  // of lanes 0-31 (k 0-7) and 32-63 (k 8-15).
+  const int g16 = lane >> 4, c16 = lane & 15, a4 = c16 & 3, j4 = c16 >> 2;
+  uint32_t abase[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      af[0][c] = *reinterpret_cast<const bf16x8*>(sA + a_row + 32 * c * kStride);
-      bfr[0][c] = *reinterpret_cast<const bf16x8*>(sB + b_row + 32 * c * kStride);
+  for (int cb = 0; cb < 4; ++cb)
+    abase[cb] = (uint32_t)((8 * (g16 >> 1) + j4) * 512 +
+                           16 * (16 * wc + 4 * (cb ^ j4) + 2 * (g16 & 1) + (a4 >> 1)) + 8 * (a4 & 1));
+  // B operand (x: 16 k x 32 tokens per MFMA): lane = token, 16 contiguous bytes
+  const int bswz = (l32 >> 1) & 7;
+  uint32_t bbase[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) bbase[ks] = (uint32_t)((128 * wt + l32) * 128 + 16 * ((2 * ks + hsel) ^ bswz));
+
+  const int nk = p.d_model / kBK;   // a multiple of 2 (d is a multiple of 256)
+  bf16x8 af[2][4], bfr[2][4];
+  auto rd = [&](const uint8_t* xs, int ks, int b) {   // operands of k-substep ks into set b
+    const uint8_t* ws = xs + kXBytes;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      typedef short v4s __attribute__((ext_vector_type(4)));
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(ws + abase[cb] + ks * 8192));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(ws + abase[cb] + ks * 8192 + 2048));
+      af[b][cb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < kBK / 16) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          af[cur ^ 1][c] = *reinterpret_cast<const bf16x8*>(sA + a_row + 32 * c * kStride + 16 * (ks + 1));
-          bfr[cur ^ 1][c] = *reinterpret_cast<const bf16x8*>(sB + b_row + 32 * c * kStride + 16 * (ks + 1));
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          acc[c][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][c], bfr[cur][t], acc[c][t], 0, 0, 0);
-    }
-    store_tiles(stage ^ 1, xreg, wreg);
-    load_tiles(min(kt + 3, nk - 1), xreg, wreg);
-    // schedule: first-step fragments; then per step its 16 MFMAs with the next step's
-    // 8 fragment reads threaded between them; LDS writes and global loads last
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (ks + 1 < kBK / 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    }
-    __syncthreads();
+    for (int tb = 0; tb < 4; ++tb)
+      bfr[b][tb] = *reinterpret_cast<const bf16x8*>(xs + bbase[ks] + tb * 4096);
   };
-  for (int kt = 0; kt < nk; kt += 2) {
-    iteration(kt, xregs[1], wregs[1]);
-    iteration(kt + 1, xregs[0], wregs[0]);
+  auto mm = [&](int b) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        acc[c][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[b][c], bfr[b][t], acc[c][t], 0, 0, 0);
+  };
+  // every wave's slices of the stage about to be read have landed, and every wave has
+  // read its operands of the other stage
+  auto sync_point = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  auto interleave = [&](int n_vmem) {     // 16 MFMAs, each with up to one load and one read
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < n_vmem) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  // Step kt reads stage kt & 1.  Its first operands were read before it starts; the
+  // barrier sits before the last k-substep's MFMAs, after which the slices of step kt + 2
+  // go into this stage and the first operands of step kt + 1 are read, both while those
+  // 16 MFMAs run.
+  auto step = [&](int kt, int stage, auto loads, auto more) {
+    const uint8_t* xs = stage ? lds1 : lds0;
+    const uint8_t* xn = stage ? lds0 : lds1;
+    __builtin_amdgcn_sched_barrier(0);
+    rd(xs, 1, 1);
+    mm(0);
+    interleave(0);
+    __builtin_amdgcn_sched_barrier(0);
+    rd(xs, 2, 0);
+    mm(1);
+    interleave(0);
+    __builtin_amdgcn_sched_barrier(0);
+    rd(xs, 3, 1);
+    mm(0);
+    interleave(0);
+    __builtin_amdgcn_sched_barrier(0);
+    sync_point();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (decltype(loads)::value) issue_loads(kt + 2, stage);
+    if constexpr (decltype(more)::value) rd(xn, 0, 0);
+    mm(1);
+    interleave(decltype(loads)::value ? 16 : 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  issue_loads(0, 0);
+  sync_point();
+  if (nk > 1) issue_loads(1, 1);
+  rd(lds0, 0, 0);
+  const std::true_type yes;
+  const std::false_type no;
+  for (int kt = 0; kt < nk - 2; kt += 2) {
+    step(kt, 0, yes, yes);
+    step(kt + 1, 1, yes, yes);
   }
+  step(nk - 2, 0, no, yes);
+  step(nk - 1, 1, no, no);
 
   // ---- epilogue: one head x 128 tokens per wave
   const int head_all = (col0 >> 7) + wc;   // head index over q | k | v
