@@ -41,7 +41,9 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=4, help="heads in the oracle's attention sample")
+    ap.add_argument("--cpu-heads", type=int, default=8, help="heads in the oracle's attention sample")
+    ap.add_argument("--cpu-query-rows", type=int, default=64, help="query rows in the oracle's attention sample")
+    ap.add_argument("--cpu-token-rows", type=int, default=256, help="token rows in the oracle's QKV-quant sample")
     ap.add_argument("--qrecompute-steps", type=int, default=1,
                     help="steps of the Q-recompute variant timed after the main steps (0 = skip)")
     ap.add_argument("--q-chunk-rows", type=int, default=0, help="query chunk of the Q-recompute variant")
@@ -333,7 +335,8 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, x, w, norm, store, args.cpu_heads)
+        result["cpu_baseline"] = cpu_baseline(wl, x, w, norm, store, args.cpu_heads, args.cpu_query_rows,
+                                              args.cpu_token_rows)
     print(json.dumps(result), flush=True)
 
 
@@ -346,10 +349,11 @@ def attention_traffic(workload):
     return MEASURED_TRAFFIC.get((sha, workload))
 
 
-def cpu_baseline(wl, x, w, norm, store, n_heads_sample):
+def cpu_baseline(wl, x, w, norm, store, n_heads_sample, n_query_rows, n_token_rows):
     """The oracle as it stands, timed on this host's cores on a bounded sample:
-    64 token rows of the QKV-quant and 8 query rows x `n_heads_sample` heads x all
-    keys of the attention.  Reported in the same unit as the GPU figure."""
+    `n_token_rows` token rows of the QKV-quant and `n_query_rows` query rows x
+    `n_heads_sample` heads x all keys of the attention (about 10-30 s of host time
+    with the defaults).  Reported in the same unit as the GPU figure."""
     import numpy as np
     import threadpoolctl
     import torch
@@ -360,7 +364,7 @@ def cpu_baseline(wl, x, w, norm, store, n_heads_sample):
     N, d, H = wl.n_tokens, wl.d_model, wl.n_heads
     dev = x.device
     extra = [b for (b, _, _) in wl.range_list()[1:]]
-    rows = synth.sample_rows(N, 64, seed=wl.seed_base + 5,
+    rows = synth.sample_rows(N, n_token_rows, seed=wl.seed_base + 5,
                              must=synth.boundary_rows(N, wl.chunk_rows, extra)[:32]).numpy()
     xb = synth.bf16_bits(x[torch.from_numpy(rows).to(dev)])
     wb = synth.bf16_bits(w)
@@ -377,7 +381,7 @@ def cpu_baseline(wl, x, w, norm, store, n_heads_sample):
     layout, _ = oracle.packed_layout(N, H, segs)
     kp, vp = store["kpack"].cpu().numpy(), store["vpack"].cpu().numpy()
     ks, vs = store["kscale"].cpu().numpy(), store["vscale"].cpu().numpy()
-    qrows = synth.sample_rows(N, 8, seed=wl.seed_base + 6).numpy()
+    qrows = synth.sample_rows(N, n_query_rows, seed=wl.seed_base + 6).numpy()
     qb = synth.bf16_bits(store["q"])[qrows]
     heads = list(range(0, H, max(1, H // n_heads_sample)))[:n_heads_sample]
     t0 = time.perf_counter()
