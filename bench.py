@@ -41,9 +41,9 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=8, help="heads in the oracle's attention sample")
+    ap.add_argument("--cpu-heads", type=int, default=24, help="heads in the oracle's attention sample")
     ap.add_argument("--cpu-query-rows", type=int, default=64, help="query rows in the oracle's attention sample")
-    ap.add_argument("--cpu-token-rows", type=int, default=256, help="token rows in the oracle's QKV-quant sample")
+    ap.add_argument("--cpu-token-rows", type=int, default=1024, help="token rows in the oracle's QKV-quant sample")
     ap.add_argument("--qrecompute-steps", type=int, default=1,
                     help="steps of the Q-recompute variant timed after the main steps (0 = skip)")
     ap.add_argument("--q-chunk-rows", type=int, default=0, help="query chunk of the Q-recompute variant")

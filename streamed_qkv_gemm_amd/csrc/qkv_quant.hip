@@ -12,8 +12,10 @@
 // (VRAM Lab page, block section `_phase1_kv`: projection -> split -> norm/RoPE ->
 // store; kvi8r section: rotated store.)
 //
-// Workgroup tile: 256 output columns (2 heads) x 256 tokens, K-step 64, four
-// waves in a 2 x 2 grid, each wave owning one head x 128 tokens.  The x and W
+// Workgroup tile: 256 output columns (2 heads) x 256 tokens, K-step 64, eight
+// waves (two per SIMD) in a 2 x 4 grid, each wave owning one head x 64 tokens
+// (128 accumulator registers), so one wave's MFMAs run through the other's
+// barrier and operand-read gaps.  The x and W
 // slices of a K-step go from HBM straight into LDS (range-checked buffer loads with
 // the LDS bit, no register staging), into two stages; W stays k-major there and
 // its MFMA operand comes out through transposing LDS reads.  One barrier per
@@ -37,6 +39,7 @@ constexpr int kBN = 256;        // tokens per workgroup
 constexpr int kBK = 64;         // reduction slice per stage
 constexpr int kXBytes = kBN * kBK * 2;          // x slice [256 tokens][64 k]: 32 KiB
 constexpr int kStageBytes = kXBytes + kBK * kBM * 2;  // + W slice [64 k][256 cols]
+constexpr int kTB = 2;          // 32-token blocks per wave (eight waves: 2 heads x 4 token quarters)
 constexpr int kGroupRows = 32;  // token tiles per raster group (L2 reuse of W and x)
 
 // RMSNorm of one head vector in column layout: u * w / sqrt(mean(u^2) + eps)
@@ -80,7 +83,7 @@ __device__ __forceinline__ void rope_cols(float (&u)[4][16], const float* __rest
     }
 }
 
-__global__ __launch_bounds__(256, 1) void qkv_quant_kernel(const QkvParams p) {
+__global__ __launch_bounds__(512, 1) void qkv_quant_kernel(const QkvParams p) {
   // two stages as two arrays, so that the compiler sees that a stage being filled and
   // the stage being read never alias (no wait on the fills before the reads)
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStageBytes];
@@ -122,40 +125,40 @@ __global__ __launch_bounds__(256, 1) void qkv_quant_kernel(const QkvParams p) {
   const __amdgpu_buffer_rsrc_t wr_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.w + col0), 0, (int32_t)0x7fffffff, kBufferWord3);
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  // wave wv moves x rows 64 wv .. + 63 and W rows 16 wv .. + 15: eight 1 KiB loads each
-  uint32_t xoff[8], woff[8];
+  // wave wv moves x rows 32 wv .. + 31 and W rows 8 wv .. + 7: four 1 KiB loads each
+  uint32_t xoff[4], woff[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int xrow = 64 * wv + 8 * i + (lane >> 3);
+  for (int i = 0; i < 4; ++i) {
+    const int xrow = 32 * wv + 8 * i + (lane >> 3);
     const int xc = (lane & 7) ^ ((xrow >> 1) & 7);
     xoff[i] = (uint32_t)(xrow * p.ldx * 2 + 16 * xc);
-    const int wrow = 16 * wv + 2 * i + (lane >> 5);
+    const int wrow = 8 * wv + 2 * i + (lane >> 5);
     const int wch = (lane & 31) ^ (4 * (wrow & 3));
     woff[i] = (uint32_t)(wrow * p.ldw * 2 + 16 * wch);
   }
   auto issue_loads = [&](int kt, int stage) {
-    uint8_t* xs = (stage ? lds1 : lds0) + wv * 8192;
+    uint8_t* xs = (stage ? lds1 : lds0) + wv * 4096;
     uint8_t* ws = xs + kXBytes;
     const uint32_t kx = (uint32_t)(kt * kBK * 2);
     const uint32_t kw = (uint32_t)((int64_t)kt * kBK * p.ldw * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr_rsrc, (__attribute__((address_space(3))) void*)(xs + 1024 * i),
                                                16, xoff[i], kx, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wr_rsrc, (__attribute__((address_space(3))) void*)(ws + 1024 * i),
                                                16, woff[i], kw, 0, 0);
   };
 
   // ---- main loop
   const int wc = wave & 1;   // column half: head 2 col_tile + wc
-  const int wt = wave >> 1;  // token half
-  f32x16 acc[4][4];
+  const int wt = wave >> 1;  // token quarter
+  f32x16 acc[4][kTB];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < kTB; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
 
@@ -173,10 +176,10 @@ __global__ __launch_bounds__(256, 1) void qkv_quant_kernel(const QkvParams p) {
   const int bswz = (l32 >> 1) & 7;
   uint32_t bbase[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) bbase[ks] = (uint32_t)((128 * wt + l32) * 128 + 16 * ((2 * ks + hsel) ^ bswz));
+  for (int ks = 0; ks < 4; ++ks) bbase[ks] = (uint32_t)((32 * kTB * wt + l32) * 128 + 16 * ((2 * ks + hsel) ^ bswz));
 
   const int nk = p.d_model / kBK;   // a multiple of 2 (d is a multiple of 256)
-  bf16x8 af[2][4], bfr[2][4];
+  bf16x8 af[2][4], bfr[2][kTB];
   auto rd = [&](const uint8_t* xs, int ks, int b) {   // operands of k-substep ks into set b
     const uint8_t* ws = xs + kXBytes;
 #pragma unroll
@@ -189,14 +192,14 @@ __global__ __launch_bounds__(256, 1) void qkv_quant_kernel(const QkvParams p) {
       af[b][cb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+    for (int tb = 0; tb < kTB; ++tb)
       bfr[b][tb] = *reinterpret_cast<const bf16x8*>(xs + bbase[ks] + tb * 4096);
   };
   auto mm = [&](int b) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < kTB; ++t)
         acc[c][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[b][c], bfr[b][t], acc[c][t], 0, 0, 0);
   };
   // every wave's slices of the stage about to be read have landed, and every wave has
@@ -207,12 +210,12 @@ __global__ __launch_bounds__(256, 1) void qkv_quant_kernel(const QkvParams p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  auto interleave = [&](int n_vmem) {     // 16 MFMAs, each with up to one load and one read
+  auto interleave = [&](int n_vmem) {     // 8 MFMAs, each with up to one load and two reads
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 4 * kTB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (i < n_vmem) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < 5) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
   // Step kt reads stage kt & 1.  Its first operands were read before it starts; the
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(256, 1) void qkv_quant_kernel(const QkvParams p) {
     if constexpr (decltype(loads)::value) issue_loads(kt + 2, stage);
     if constexpr (decltype(more)::value) rd(xn, 0, 0);
     mm(1);
-    interleave(decltype(loads)::value ? 16 : 0);
+    interleave(decltype(loads)::value ? 8 : 0);
     __builtin_amdgcn_sched_barrier(0);
   };
   issue_loads(0, 0);
@@ -260,33 +263,24 @@ __global__ __launch_bounds__(256, 1) void qkv_quant_kernel(const QkvParams p) {
   const int head_all = (col0 >> 7) + wc;   // head index over q | k | v
   const int section = head_all / p.n_heads;  // 0 q, 1 k, 2 v
   const int h = head_all - section * p.n_heads;
-  const int64_t wtok0 = tok0 + 128 * wt;
+  const int64_t wtok0 = tok0 + 32 * kTB * wt;
   if (wtok0 >= p.row_end) return;          // wave-uniform
   const int seg = find_segment(p.seg, wtok0);
   const int fmt = head_format(p.seg, seg, h);
   const int64_t head_base = head_rows_offset(p.seg, seg, h);
   const int row_bytes = format_row_bytes(fmt);
 
-  // The token-block loop stays rolled (its body is large); the accumulator column
-  // is picked with static indices so the accumulators never leave registers.
-#pragma nounroll
-  for (int tb = 0; tb < 4; ++tb) {
+  // The two token blocks are unrolled, so the first block's accumulators are free
+  // registers while the second is processed (rolled, both stay live and spill).
+#pragma unroll
+  for (int tb = 0; tb < kTB; ++tb) {
     const int64_t t = wtok0 + 32 * tb + l32;
     const bool valid = t < p.row_end;
     float u[4][16];
-    switch (tb) {
-#define SQG_TAKE_COLUMN(TB)                                    \
-      case TB:                                                 \
-        _Pragma("unroll") for (int b = 0; b < 4; ++b)          \
-        _Pragma("unroll") for (int i = 0; i < 16; ++i) u[b][i] = acc[b][TB][i]; \
-        break;
-      SQG_TAKE_COLUMN(0)
-      SQG_TAKE_COLUMN(1)
-      SQG_TAKE_COLUMN(2)
-      default:
-      SQG_TAKE_COLUMN(3)
-#undef SQG_TAKE_COLUMN
-    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) u[b][i] = acc[b][tb][i];
 
     if (section == 0) {
       if (p.q_norm_w) rms_norm_cols(u, p.q_norm_w, p.eps);
@@ -335,7 +329,7 @@ int launch_qkv_quant(const QkvParams& p, void* stream) {
   const int64_t n_tok_tiles = (rows + kBN - 1) / kBN;
   const int64_t blocks = n_tok_tiles * p.n_col_tiles;
   if (blocks <= 0) return 0;
-  hipLaunchKernelGGL(qkv_quant_kernel, dim3((unsigned)blocks), dim3(256), 0,
+  hipLaunchKernelGGL(qkv_quant_kernel, dim3((unsigned)blocks), dim3(512), 0,
                      (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
