@@ -19,7 +19,7 @@
 // slices of a K-step go from HBM straight into LDS (range-checked buffer loads with
 // the LDS bit, no register staging), into two stages; W stays k-major there and
 // its MFMA operand comes out through transposing LDS reads.  One barrier per
-// K-step sits before the step's last k-substep, whose 16 MFMAs then run beside the
+// K-step sits before the step's last k-substep, whose 8 MFMAs per wave run beside the
 // loads of the slices two steps ahead and the next step's first operand reads;
 // scheduling groups thread each substep's operand reads between the MFMAs of the
 // substep before.  The transposed
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(512, 1) void qkv_quant_kernel(const QkvParams p) {
   // Step kt reads stage kt & 1.  Its first operands were read before it starts; the
   // barrier sits before the last k-substep's MFMAs, after which the slices of step kt + 2
   // go into this stage and the first operands of step kt + 1 are read, both while those
-  // 16 MFMAs run.
+  // MFMAs (8 per wave) run.
   auto step = [&](int kt, int stage, auto loads, auto more) {
     const uint8_t* xs = stage ? lds1 : lds0;
     const uint8_t* xn = stage ? lds0 : lds1;
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(512, 1) void qkv_quant_kernel(const QkvParams p) {
   step(nk - 2, 0, no, yes);
   step(nk - 1, 1, no, no);
 
-  // ---- epilogue: one head x 128 tokens per wave
+  // ---- epilogue: one head x 64 tokens per wave
   const int head_all = (col0 >> 7) + wc;   // head index over q | k | v
   const int section = head_all / p.n_heads;  // 0 q, 1 k, 2 v
   const int h = head_all - section * p.n_heads;
