@@ -244,7 +244,7 @@ def main():
                       "qkv_quant_to_host_ms": b_ms, "attention_from_host_ms": a_ms,
                       "host_store_bytes": 2 * (hp + hs), "device_staging_bytes": 4 * (dp + ds),
                       "device_kv_bytes_vs_device_store": 4 * (dp + ds) / (2 * (hp + hs)),
-                      "copies": "synchronous order on the compute stream (no copy/compute overlap)"}
+                      "copies": "on a stream of their own, ordered by events against the kernels (overlapped)"}
         del stg, q_st
         torch.cuda.empty_cache()
 

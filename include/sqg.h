@@ -36,7 +36,7 @@ extern "C" {
 #define SQG_API
 #endif
 
-#define SQG_VERSION 130          /* 1.3.0 */
+#define SQG_VERSION 131          /* 1.3.1 */
 #define SQG_HEAD_DIM 128
 #define SQG_GROUP 32
 #define SQG_MAX_SEGMENTS 16
@@ -189,7 +189,15 @@ typedef struct sqg_attn_args {
  * (sqg_kv_block_layout) whose codes start at host_kpack + (sum of the pack_bytes of
  * blocks before b), and whose scales start at host_kscale + (sum of their scale_bytes);
  * likewise for V.  Two device staging block stores carry blocks between host and
- * kernels.  sqg_staged_sizes gives every buffer size. */
+ * kernels.  sqg_staged_sizes gives every buffer size.  With copy_stream NULL the copies
+ * run in order on the call's stream; with a second stream (default priority, same
+ * device) they run there, ordered against the kernels by events, so a block's copy
+ * overlaps the neighbouring block's kernel (a staging slot is refilled only after the
+ * kernel that used it, a kernel starts only after its block's copy).  The copy stream
+ * first waits for the work already on the call's stream, and a staged QKV-quant call
+ * leaves the call's stream waiting for its last copies, so either way the caller sees
+ * the same ordering as with in-order copies.  Calls that share one copy stream must not
+ * overlap in time. */
 typedef struct sqg_staged_kv {
   int64_t block_rows;          /* keys per block, a positive multiple of 128 */
   void* host_kpack;            /* pinned host (hipHostMalloc / pinned torch tensors) */
@@ -200,6 +208,7 @@ typedef struct sqg_staged_kv {
   void* dev_vpack[2];
   void* dev_kscale[2];
   void* dev_vscale[2];
+  void* copy_stream;           /* hipStream_t for the copies, or NULL (copies in order) */
 } sqg_staged_kv;
 
 /* Arguments of sqg_packed_kv_attention_qrecompute. */

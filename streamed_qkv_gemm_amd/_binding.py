@@ -75,7 +75,8 @@ class AttnArgs(ctypes.Structure):
 class StagedKV(ctypes.Structure):
     _fields_ = [("block_rows", _c_i64), ("host_kpack", _vp), ("host_vpack", _vp),
                 ("host_kscale", _vp), ("host_vscale", _vp), ("dev_kpack", _vp * 2),
-                ("dev_vpack", _vp * 2), ("dev_kscale", _vp * 2), ("dev_vscale", _vp * 2)]
+                ("dev_vpack", _vp * 2), ("dev_kscale", _vp * 2), ("dev_vscale", _vp * 2),
+                ("copy_stream", _vp)]
 
 
 class QRecomputeArgs(ctypes.Structure):
@@ -389,9 +390,11 @@ def staged_sizes(n_tokens: int, d_model: int, block_rows: int, ranges=None):
     return tuple(sizes), nb.value
 
 
-def alloc_staged(n_tokens: int, d_model: int, block_rows: int, ranges=None, device="cuda") -> Dict:
+def alloc_staged(n_tokens: int, d_model: int, block_rows: int, ranges=None, device="cuda",
+                 overlap: bool = True) -> Dict:
     """A host-staged K/V store: pinned host buffers for every block, two device staging
-    block stores, and the block plan."""
+    block stores, the block plan, and (overlap) a stream of default priority on which the
+    copies run beside the kernels."""
     (hp, hs, dp, ds), nb = staged_sizes(n_tokens, d_model, block_rows, ranges)
     pinned = lambda n: torch.empty((max(n, 16),), dtype=torch.uint8, pin_memory=True)  # noqa: E731
     dev = lambda n: torch.empty((max(n, 16),), dtype=torch.uint8, device=device)  # noqa: E731
@@ -400,7 +403,8 @@ def alloc_staged(n_tokens: int, d_model: int, block_rows: int, ranges=None, devi
           "host_kpack": pinned(hp), "host_vpack": pinned(hp), "host_kscale": pinned(hs),
           "host_vscale": pinned(hs),
           "dev_kpack": [dev(dp), dev(dp)], "dev_vpack": [dev(dp), dev(dp)],
-          "dev_kscale": [dev(ds), dev(ds)], "dev_vscale": [dev(ds), dev(ds)]}
+          "dev_kscale": [dev(ds), dev(ds)], "dev_vscale": [dev(ds), dev(ds)],
+          "copy_stream": torch.cuda.Stream(device=device) if overlap else None}
     return st
 
 
@@ -416,6 +420,8 @@ def _staged_struct(st: Dict) -> StagedKV:
         arr = getattr(s, k)
         for i in range(2):
             arr[i] = _dev_ptr(st[k][i], k)
+    cs = st.get("copy_stream")
+    s.copy_stream = cs.cuda_stream if cs is not None else None
     return s
 
 

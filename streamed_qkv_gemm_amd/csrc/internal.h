@@ -84,4 +84,10 @@ const char* hip_error_text(int err);
 enum CopyKind { kHostToDevice = 1, kDeviceToHost = 2 };
 int copy_async(void* dst, const void* src, int64_t bytes, CopyKind kind, void* stream);
 
+// Events ordering work across two streams (timing disabled); each returns a hipError_t value.
+int event_create(void** ev);
+int event_destroy(void* ev);
+int event_record(void* ev, void* stream);
+int stream_wait_event(void* stream, void* ev);
+
 }  // namespace sqg

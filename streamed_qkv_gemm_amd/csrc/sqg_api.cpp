@@ -219,6 +219,43 @@ int launch_status(int hip_err, const char* what) {
   return SQG_OK;
 }
 
+// Events of one staged call with a copy stream: the entry point on the call's stream,
+// and per staging slot the kernel that last used it and its last copy.  Destroyed on
+// return, pending or not (the runtime releases them once they complete).
+struct StageEvents {
+  void* ev[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+  ~StageEvents() {
+    for (void* e : ev) sqg::event_destroy(e);
+  }
+  int create() {
+    for (void*& e : ev) {
+      const int r = sqg::event_create(&e);
+      if (r) return r;
+    }
+    return 0;
+  }
+  void* start() const { return ev[0]; }
+  void* kernel(int slot) const { return ev[1 + slot]; }
+  void* copy(int slot) const { return ev[3 + slot]; }
+};
+
+// With a copy stream: create the events and let the copy stream wait for the work
+// already enqueued on the call's stream.
+int stage_begin(StageEvents& E, void* copy_stream, void* stream) {
+  int st = launch_status(E.create(), "staging events");
+  if (st != SQG_OK) return st;
+  st = launch_status(sqg::event_record(E.start(), stream), "staging event record");
+  if (st != SQG_OK) return st;
+  return launch_status(sqg::stream_wait_event(copy_stream, E.start()), "staging stream wait");
+}
+
+// `waiter` waits for `ev` after recording it on `recorder` (no-op without a copy stream)
+int stage_order(void* ev, void* recorder, void* waiter) {
+  int st = launch_status(sqg::event_record(ev, recorder), "staging event record");
+  if (st != SQG_OK) return st;
+  return launch_status(sqg::stream_wait_event(waiter, ev), "staging stream wait");
+}
+
 // Checks the attention arguments and fills the kernel parameters.  With check_q false
 // the caller supplies Q itself (a->q and a->ldq are ignored).  *empty is set when there
 // is nothing to compute.
@@ -649,9 +686,20 @@ SQG_API int sqg_streamed_qkv_quant_staged(const sqg_qkv_args* a, const sqg_stage
   st = staged_plan(L, a->d_model, sk->block_rows, &blocks);
   if (st != SQG_OK) return st;
   if (empty) return ok();
+  void* const cs = sk->copy_stream;
+  void* const copy_stream = cs ? cs : stream;
+  StageEvents E;
+  if (cs) {
+    st = stage_begin(E, cs, stream);
+    if (st != SQG_OK) return st;
+  }
   for (size_t i = 0; i < blocks.size(); ++i) {
     const StagedBlock& b = blocks[i];
     const int j = (int)(i & 1);
+    if (cs && i >= 2) {   // slot j's previous block has left the device
+      st = launch_status(sqg::stream_wait_event(stream, E.copy(j)), "staging stream wait");
+      if (st != SQG_OK) return st;
+    }
     p.kpack = static_cast<uint8_t*>(sk->dev_kpack[j]);
     p.vpack = static_cast<uint8_t*>(sk->dev_vpack[j]);
     p.kscale = static_cast<uint16_t*>(sk->dev_kscale[j]);
@@ -663,17 +711,31 @@ SQG_API int sqg_streamed_qkv_quant_staged(const sqg_qkv_args* a, const sqg_stage
     p.row_end = b.k1;
     st = launch_status(sqg::launch_qkv_quant(p, stream), "streamed_qkv_quant launch");
     if (st != SQG_OK) return st;
+    if (cs) {   // the copies start once this block's kernel is done
+      st = stage_order(E.kernel(j), stream, cs);
+      if (st != SQG_OK) return st;
+    }
     char* hk = static_cast<char*>(sk->host_kpack) + b.pack_off;
     char* hv = static_cast<char*>(sk->host_vpack) + b.pack_off;
     char* hks = static_cast<char*>(sk->host_kscale) + b.scale_off;
     char* hvs = static_cast<char*>(sk->host_vscale) + b.scale_off;
     const int rc[4] = {
-        sqg::copy_async(hk, sk->dev_kpack[j], b.L.pack_bytes, sqg::kDeviceToHost, stream),
-        sqg::copy_async(hv, sk->dev_vpack[j], b.L.pack_bytes, sqg::kDeviceToHost, stream),
-        sqg::copy_async(hks, sk->dev_kscale[j], b.L.scale_bytes, sqg::kDeviceToHost, stream),
-        sqg::copy_async(hvs, sk->dev_vscale[j], b.L.scale_bytes, sqg::kDeviceToHost, stream)};
+        sqg::copy_async(hk, sk->dev_kpack[j], b.L.pack_bytes, sqg::kDeviceToHost, copy_stream),
+        sqg::copy_async(hv, sk->dev_vpack[j], b.L.pack_bytes, sqg::kDeviceToHost, copy_stream),
+        sqg::copy_async(hks, sk->dev_kscale[j], b.L.scale_bytes, sqg::kDeviceToHost, copy_stream),
+        sqg::copy_async(hvs, sk->dev_vscale[j], b.L.scale_bytes, sqg::kDeviceToHost, copy_stream)};
     for (int r : rc) {
       st = launch_status(r, "staging copy to host");
+      if (st != SQG_OK) return st;
+    }
+    if (cs) {
+      st = launch_status(sqg::event_record(E.copy(j), cs), "staging event record");
+      if (st != SQG_OK) return st;
+    }
+  }
+  if (cs) {   // the call's stream continues once the host store is complete
+    for (size_t j = 0; j < blocks.size() && j < 2; ++j) {
+      st = launch_status(sqg::stream_wait_event(stream, E.copy((int)j)), "staging stream wait");
       if (st != SQG_OK) return st;
     }
   }
@@ -710,20 +772,35 @@ SQG_API int sqg_packed_kv_attention_staged(const sqg_attn_args* a, const sqg_sta
   if (meet.size() > 1 && (!a->lse || a->o_dtype != SQG_F32))
     return fail(SQG_ERR_INVALID_ARGUMENT, "the key range spans %d blocks: merging needs an lse buffer and o_dtype SQG_F32",
                 (int)meet.size());
+  void* const cs = sk->copy_stream;
+  void* const copy_stream = cs ? cs : stream;
+  StageEvents E;
+  if (cs && !meet.empty()) {
+    st = stage_begin(E, cs, stream);
+    if (st != SQG_OK) return st;
+  }
   for (size_t i = 0; i < meet.size(); ++i) {
     const StagedBlock& b = *meet[i];
     const int j = (int)(i & 1);
+    if (cs && i >= 2) {   // the kernel that read slot j (two blocks back) is done
+      st = launch_status(sqg::stream_wait_event(cs, E.kernel(j)), "staging stream wait");
+      if (st != SQG_OK) return st;
+    }
     const char* hk = static_cast<const char*>(sk->host_kpack) + b.pack_off;
     const char* hv = static_cast<const char*>(sk->host_vpack) + b.pack_off;
     const char* hks = static_cast<const char*>(sk->host_kscale) + b.scale_off;
     const char* hvs = static_cast<const char*>(sk->host_vscale) + b.scale_off;
     const int rc[4] = {
-        sqg::copy_async(sk->dev_kpack[j], hk, b.L.pack_bytes, sqg::kHostToDevice, stream),
-        sqg::copy_async(sk->dev_vpack[j], hv, b.L.pack_bytes, sqg::kHostToDevice, stream),
-        sqg::copy_async(sk->dev_kscale[j], hks, b.L.scale_bytes, sqg::kHostToDevice, stream),
-        sqg::copy_async(sk->dev_vscale[j], hvs, b.L.scale_bytes, sqg::kHostToDevice, stream)};
+        sqg::copy_async(sk->dev_kpack[j], hk, b.L.pack_bytes, sqg::kHostToDevice, copy_stream),
+        sqg::copy_async(sk->dev_vpack[j], hv, b.L.pack_bytes, sqg::kHostToDevice, copy_stream),
+        sqg::copy_async(sk->dev_kscale[j], hks, b.L.scale_bytes, sqg::kHostToDevice, copy_stream),
+        sqg::copy_async(sk->dev_vscale[j], hvs, b.L.scale_bytes, sqg::kHostToDevice, copy_stream)};
     for (int r : rc) {
       st = launch_status(r, "staging copy to device");
+      if (st != SQG_OK) return st;
+    }
+    if (cs) {   // this block's kernel starts once its copies have landed
+      st = stage_order(E.copy(j), cs, stream);
       if (st != SQG_OK) return st;
     }
     p.kpack = static_cast<const uint8_t*>(sk->dev_kpack[j]);
@@ -738,6 +815,10 @@ SQG_API int sqg_packed_kv_attention_staged(const sqg_attn_args* a, const sqg_sta
     p.accumulate = i == 0 ? a->accumulate : 1;
     st = launch_status(sqg::launch_packed_attention(p, stream), "packed_kv_attention launch");
     if (st != SQG_OK) return st;
+    if (cs) {
+      st = launch_status(sqg::event_record(E.kernel(j), stream), "staging event record");
+      if (st != SQG_OK) return st;
+    }
   }
   return ok();
 }

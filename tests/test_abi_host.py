@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 10
     for n in names:
         assert hasattr(lib, n), n
-    assert sqg.version() == 130
+    assert sqg.version() == 131
 
 
 def test_struct_sizes_match_binding():

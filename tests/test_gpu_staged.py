@@ -145,3 +145,24 @@ def test_staged_attention_subranges_and_accumulate(lib):
                                    o=o, lse=l)
     torch.cuda.synchronize()
     assert torch.equal(o, o_ref) and torch.equal(l, l_ref)
+
+
+def test_overlapped_and_in_order_copies_agree(lib):
+    # the copies on a stream of their own (the default) and in order on the call's stream
+    # must leave the same host bytes and give the same attention, block for block
+    x, w, kw = make(lib, 341)
+    full = lib.streamed_qkv_quant(x, w, ranges=POLICY, **kw)
+    a = lib.alloc_staged(N, D, 512, POLICY, device=DEV)
+    b = lib.alloc_staged(N, D, 512, POLICY, device=DEV, overlap=False)
+    assert a["copy_stream"] is not None and b["copy_stream"] is None
+    lib.streamed_qkv_quant_staged(x, w, a, emit=lib.SQG_EMIT_KV, **kw)
+    lib.streamed_qkv_quant_staged(x, w, b, emit=lib.SQG_EMIT_KV, **kw)
+    oa, la = lib.packed_kv_attention_staged(a, full["q"])
+    ob, lb = lib.packed_kv_attention_staged(b, full["q"])
+    # back to back on the same stream: the second call's copies follow the first's kernels
+    oa2, la2 = lib.packed_kv_attention_staged(a, full["q"])
+    torch.cuda.synchronize()
+    for k in ("host_kpack", "host_vpack", "host_kscale", "host_vscale"):
+        assert torch.equal(a[k], b[k]), k
+    assert torch.equal(oa, ob) and torch.equal(la, lb)
+    assert torch.equal(oa2, oa) and torch.equal(la2, la)
