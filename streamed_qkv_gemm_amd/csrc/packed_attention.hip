@@ -447,7 +447,6 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
         kf[b][kb] = *reinterpret_cast<const f16x8*>(K + (32 * kb + l32) * kKStride + 16 * ks + 8 * hsel);
     };
     rd(0, 0);
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       if (ks < 7) rd(ks + 1, (ks + 1) & 1);
@@ -457,7 +456,6 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks & 1][kb], qf[ks], acc, 0, 0, 0);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks & 1][kb], lo[ks & 1], s[kb], 0, 0, 0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -547,14 +545,12 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
       }
     };
     rd(0, 0);
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < 2 * kKB; ++ks) {
       if (ks + 1 < 2 * kKB) rd(ks + 1, (ks + 1) & 1);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[ks & 1][db], pf[ks], oacc[db], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
