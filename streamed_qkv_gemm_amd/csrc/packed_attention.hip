@@ -30,8 +30,9 @@
 // lane pair, so the softmax statistics and the final inverse rotation are
 // register-local apart from one exchange with lane ^ 32 (v_permlane32_swap inside
 // the loop).  The query's high part stays in registers; its remainder waits in LDS
-// next to the tiles, and both K and V fragments are read one MFMA step ahead into
-// a second register set, so the LDS latency hides behind the running MFMAs.  The running maximum is
+// next to the tiles; the K and V fragment reads sit in plain loops next to their
+// MFMAs and the compiler places them ahead (explicit double-buffered prefetch and
+// scheduling fences measured 1-2% slower).  The running maximum is
 // only moved (and O rescaled) when a column's maximum grows by more than 2^8, so
 // most tiles skip the rescale; P then stays below 256, well inside f16.
 #include "device_common.h"
@@ -438,23 +439,15 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
 
   auto do_qk = [&](int stage, f32x16 (&s)[kKB]) {
     const _Float16* K = sK[stage];
-    // fragments of k-step ks+1 are read while the four MFMAs of step ks run
-    f16x8 kf[2][kKB], lo[2];
-    auto rd = [&](int ks, int b) {
-      lo[b] = *reinterpret_cast<const f16x8*>(qlw + (ks * 64 + lane) * 8);
-#pragma unroll
-      for (int kb = 0; kb < kKB; ++kb)
-        kf[b][kb] = *reinterpret_cast<const f16x8*>(K + (32 * kb + l32) * kKStride + 16 * ks + 8 * hsel);
-    };
-    rd(0, 0);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      if (ks < 7) rd(ks + 1, (ks + 1) & 1);
+      const f16x8 lo = *reinterpret_cast<const f16x8*>(qlw + (ks * 64 + lane) * 8);
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb) {
+        const f16x8 kf = *reinterpret_cast<const f16x8*>(K + (32 * kb + l32) * kKStride + 16 * ks + 8 * hsel);
         const f32x16 acc = ks == 0 ? f32x16{} : s[kb];
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks & 1][kb], qf[ks], acc, 0, 0, 0);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks & 1][kb], lo[ks & 1], s[kb], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], acc, 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, lo, s[kb], 0, 0, 0);
       }
     }
   };
@@ -525,7 +518,6 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
 
   auto do_pv = [&](int stage, const f16x8 (&pf)[2 * kKB]) {
     const _Float16* V = sV[stage];
-    f16x8 vf[2][4];
     // A operand (V^T) by transposing LDS reads: lane L gets dim 32 db + L % 32 of keys
     // 16 ks + 4 hsel + 0..3 and 16 ks + 8 + 4 hsel + 0..3 (the MFMA's k slots 8 hsel + e
     // with bits 2 and 3 swapped, matching the key order of the P operand).  Each 16-lane
@@ -536,21 +528,15 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
     const int vd = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     const _Float16* vb0 = V + vk * kVStride + vcol(vk, vd);
     const _Float16* vb1 = V + (vk + 8) * kVStride + vcol(vk + 8, vd);
-    auto rd = [&](int ks, int b) {
+#pragma unroll
+    for (int ks = 0; ks < 2 * kKB; ++ks) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const f16x4 lo = tr_read_f16x4(vb0 + 16 * ks * kVStride + 32 * db);
         const f16x4 hi = tr_read_f16x4(vb1 + 16 * ks * kVStride + 32 * db);
-        vf[b][db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const f16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[ks], oacc[db], 0, 0, 0);
       }
-    };
-    rd(0, 0);
-#pragma unroll
-    for (int ks = 0; ks < 2 * kKB; ++ks) {
-      if (ks + 1 < 2 * kKB) rd(ks + 1, (ks + 1) & 1);
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[ks & 1][db], pf[ks], oacc[db], 0, 0, 0);
     }
   };
 
