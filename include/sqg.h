@@ -366,17 +366,6 @@ SQG_API int sqg_test_quant_pack_f32(const float* r, int64_t rows, int32_t fmt, v
 SQG_API int sqg_test_fwht_f32(const float* in, float* out, int64_t rows, int32_t normalize,
                               void* stream);
 
-/* Measurement entry (no part of the method): a kernel that only issues matrix-core
- * instructions, for the rate the device sustains under a pure MFMA load, against
- * which the two kernels' MFMA utilisation can be read besides the published peak.
- * n_blocks workgroups of 256 threads; every wave runs `iters` rounds of four
- * independent 32x32x16 MFMAs (dtype 0: f16 operands, 1: bf16; fp32 accumulation),
- * i.e. n_blocks * 4 * iters * 4 * 32768 flop, and writes one float per thread to
- * sink (device, n_blocks * 256 floats, 16-byte aligned).  Enqueued on `stream`;
- * time it with events around the call.  iters > 0, n_blocks > 0. */
-SQG_API int sqg_test_mfma_rate(int32_t dtype, int64_t iters, int64_t n_blocks, float* sink,
-                               void* stream);
-
 #ifdef __cplusplus
 }
 #endif

@@ -16,8 +16,8 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
-    "HEAD_DIM", "GROUP", "INT4", "INT8", "BF16", "FORMATS", "QMAX", "ROW_BYTES", "SCALE_BITS",
-    "round_up_bits", "segment_parts", "head_formats", "gather_bf16_rows",
+    "HEAD_DIM", "GROUP", "INT4", "INT8", "BF16", "FORMATS", "QMAX", "ROW_BYTES", "INT4_SCALE_BITS",
+    "INT8_SCALE_FACTOR", "round_up_bits", "group_scales", "segment_parts", "head_formats", "gather_bf16_rows",
     "hadamard_pm1", "rotation_matrix",
     "f32_to_bf16_bits", "bf16_bits_to_f64", "f32_to_f16",
     "chunk_ranges", "range_segments", "token_formats",
@@ -40,9 +40,13 @@ BF16 = 2                # rotated INT4)
 FORMATS = (INT4, INT8, BF16)
 QMAX = {INT4: 7, INT8: 127}
 ROW_BYTES = {INT4: HEAD_DIM // 2, INT8: HEAD_DIM, BF16: 2 * HEAD_DIM}
-# significant bits kept in a group scale: code bits + scale bits <= 11, so code * scale
-# is exact in fp16 (INT4 codes need 3 bits, INT8 codes 7)
-SCALE_BITS = {INT4: 8, INT8: 4}
+# INT4 group scales keep 8 significant bits (rounded up), so that code * scale is exact in
+# fp16 (3 code bits + 8 scale bits = 11): the attention kernel decodes INT4 without rounding
+INT4_SCALE_BITS = 8
+# INT8 group scales follow [VL] kvi8r `_Int8KV.store`: the absmax times 1/127 enlarged by
+# (1 + 2^-7) so that the fp16 rounding of the scale can never push a code past 127.  The
+# page multiplies an fp32 tensor by a Python float, i.e. by that constant rounded to fp32.
+INT8_SCALE_FACTOR = np.float32(1.0 / 127.0 * (1.0 + 2.0 ** -7))
 
 
 # --------------------------------------------------------------------------- rotation
@@ -85,17 +89,20 @@ def f32_to_f16(x) -> np.ndarray:
 
 # --------------------------------------------------------------------------- chunk plan and range policy
 def chunk_ranges(n: int, size: int, min_tail: int = 512) -> List[Tuple[int, int]]:
-    """Row chunks of `size` rows; a last chunk shorter than `min_tail` is folded into
-    the one before it.  size <= 0 or size >= n gives one chunk.
+    """Row chunks of `size` rows over [0, n); a remainder shorter than `min_tail` rows
+    joins the last full chunk.  size <= 0 or size >= n gives one chunk.
 
-    [VL] helpers section, `_ranges`."""
+    The rule of the [VL] helpers section (`_ranges`), computed from the counts: n rows
+    make n // size full chunks and a remainder of n % size rows; the remainder is a
+    chunk of its own unless it is shorter than min_tail, in which case the last full
+    chunk runs on to n."""
     if size <= 0 or size >= n:
         return [(0, n)]
-    out = [(a, min(a + size, n)) for a in range(0, n, size)]
-    if len(out) > 1 and out[-1][1] - out[-1][0] < min_tail:
-        out.pop()
-        out[-1] = (out[-1][0], n)
-    return out
+    n_full, rest = divmod(n, size)
+    n_chunks = n_full + (1 if rest >= max(min_tail, 1) else 0)
+    starts = [size * i for i in range(n_chunks)]
+    ends = starts[1:] + [n]
+    return list(zip(starts, ends))
 
 
 def range_segments(n: int, ranges: Optional[Sequence[Tuple[int, int, int]]],
@@ -241,26 +248,39 @@ def round_up_bits(t: np.ndarray, bits: int) -> np.ndarray:
     return u.astype(np.uint32).view(np.float32)
 
 
+def group_scales(a: np.ndarray, qmax: int) -> np.ndarray:
+    """fp16 scale of each group from its fp32 absmax a.
+
+    INT4 (qmax 7): t = a / 7 in IEEE fp32, rounded UP to INT4_SCALE_BITS significant
+    bits, stored as fp16 (exact).  The round-up enlarges the step by less than 2^-7,
+    the page's own enlargement factor for its int8 scale.  [VL] precision-probe
+    section, `_fq_int4` (absmax / 7).
+    INT8 (qmax 127): s = fp16_RNE(fp32(a * INT8_SCALE_FACTOR)), the scale rule of [VL]
+    kvi8r `_Int8KV.store` (absmax * (1/127) * (1 + 2^-7) in fp32, then cast to the
+    16-bit store dtype)."""
+    a = np.asarray(a, dtype=np.float32)
+    if qmax == QMAX[INT4]:
+        return round_up_bits((a / np.float32(qmax)).astype(np.float32), INT4_SCALE_BITS).astype(np.float16)
+    if qmax == QMAX[INT8]:
+        return (a * INT8_SCALE_FACTOR).astype(np.float32).astype(np.float16)
+    raise ValueError("qmax must be 7 (INT4) or 127 (INT8)")
+
+
 def quantize_groups(r: np.ndarray, qmax: int):
     """Group quantisation of fp32 rotated vectors [..., 128] in groups of 32.
 
-    For each group: a = max |r| (fp32); t = a / qmax in IEEE fp32; the scale s is t
-    rounded UP to SCALE_BITS significant bits, stored as fp16; if s == 0 every code
-    is 0; otherwise c = clamp(rne(r / fp32(s)), -qmax, qmax) with
+    For each group: a = max |r| (fp32); s = `group_scales(a, qmax)` (fp16); if s == 0
+    every code is 0; otherwise c = clamp(rne(r / fp32(s)), -qmax, qmax) with
     round-half-to-even and IEEE fp32 division.
     [VL] precision-probe section, `_fq_int4` (absmax / 7, round, clamp) and kvi8r
-    `_Int8KV.store` (absmax / 127 with the scale rounded UP so codes stay within
-    +-127); the workloads give group 32 along head_dim and fp16 scales.  Reading:
-    the scale keeps few enough bits that code * scale is exact in fp16 (8 bits for
-    INT4, 4 for INT8, rounded up as the page rounds its int8 scale up).
+    `_Int8KV.store` (scale from absmax / 127, torch.round, clamp to +-127); the
+    workloads give group 32 along head_dim and fp16 scales.
     Returns (codes int8, scales fp16)."""
     r = np.ascontiguousarray(np.asarray(r, dtype=np.float32))
     lead = r.shape[:-1]
     g = r.reshape(lead + (HEAD_DIM // GROUP, GROUP))
     a = np.max(np.abs(g), axis=-1)                                  # fp32, exact
-    bits = 8 if qmax == QMAX[INT4] else 4
-    t = (a / np.float32(qmax)).astype(np.float32)
-    s16 = round_up_bits(t, bits).astype(np.float16)
+    s16 = group_scales(a, qmax)
     s32 = s16.astype(np.float32)
     safe = np.where(s32 == 0, np.float32(1), s32)
     q = np.rint(g / safe[..., None])                                # fp32 division, RNE

@@ -10,6 +10,6 @@ from ._binding import (  # noqa: F401
     SQG_BF16_ROT, SQG_INT4_ROT, SQG_INT8_ROT, SqgError, alloc_store, chunk_ranges, kv_layout, lib_path, load,
     alloc_staged, kv_block_layout, kv_row_offset, packed_kv_attention, packed_kv_attention_qrecompute,
     packed_kv_attention_staged, qrecompute_workspace_bytes, rope_table, staged_sizes,
-    streamed_qkv_quant, streamed_qkv_quant_staged, test_fwht_f32, test_mfma_rate, test_quant_pack_f32,
+    streamed_qkv_quant, streamed_qkv_quant_staged, test_fwht_f32, test_quant_pack_f32,
     version,
 )

@@ -125,7 +125,6 @@ def load(path: Optional[str] = None):
     lib.sqg_packed_kv_attention_qrecompute.argtypes = [ctypes.POINTER(QRecomputeArgs), _vp]
     lib.sqg_test_quant_pack_f32.argtypes = [_vp, _c_i64, _c_i32, _vp, _vp, _vp]
     lib.sqg_test_fwht_f32.argtypes = [_vp, _vp, _c_i64, _c_i32, _vp]
-    lib.sqg_test_mfma_rate.argtypes = [_c_i32, _c_i64, _c_i64, _vp, _vp]
     for name, cls in ((0, Range), (1, Layout), (2, QkvArgs), (3, AttnArgs), (4, QRecomputeArgs),
                       (5, StagedKV)):
         got = lib.sqg_struct_size(name)
@@ -501,26 +500,3 @@ def test_fwht_f32(x: torch.Tensor, normalize: bool = False):
     _check(lib.sqg_test_fwht_f32(_dev_ptr(x, "x"), out.data_ptr(), x.shape[0], int(normalize),
                                  _stream(x.device)))
     return out
-
-
-def test_mfma_rate(dtype: int = 0, iters: int = 20000, blocks_per_cu: int = 2, repeats: int = 3,
-                   device="cuda"):
-    """Sustained matrix-core rate (TFLOP/s, best of `repeats` timed launches) of a kernel
-    that issues only 32x32x16 MFMAs (dtype 0 f16, 1 bf16), blocks_per_cu workgroups of
-    four waves per compute unit."""
-    lib = load()
-    dev = torch.device(device)
-    n_blocks = blocks_per_cu * torch.cuda.get_device_properties(dev).multi_processor_count
-    sink = torch.empty(n_blocks * 256, dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    _check(lib.sqg_test_mfma_rate(dtype, 64, n_blocks, sink.data_ptr(), stream.cuda_stream))
-    best = float("inf")
-    for _ in range(repeats):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        _check(lib.sqg_test_mfma_rate(dtype, iters, n_blocks, sink.data_ptr(), stream.cuda_stream))
-        e1.record(stream)
-        e1.synchronize()
-        best = min(best, e0.elapsed_time(e1))
-    flop = n_blocks * 4 * iters * 4 * 32768.0
-    return flop / (best * 1e-3) / 1e12

@@ -109,10 +109,30 @@ __device__ __forceinline__ void fwht128_cols(float (&u)[4][16]) {
 }
 
 // ----------------------------------------------------------------------------- quantise + pack
+// The group scales of the two integer formats, from a group's fp32 absmax a:
+//   INT4: a / 7 (IEEE fp32 division) rounded UP to 8 significant bits, stored as fp16
+//     (exact).  Three code bits plus eight scale bits fit fp16's eleven, so the
+//     attention kernel's f16 decode code * scale is exact for INT4 tiles; the round-up
+//     enlarges the step by less than 2^-7, the page's own enlargement of its int8 scale.
+//   INT8: VRAM Lab page, kvi8r section (`_Int8KV.store`): a * fp32((1 + 2^-7) / 127) in
+//     fp32, rounded to nearest fp16.  The enlargement keeps |r / s| below 127 whatever
+//     the fp16 rounding does.
+constexpr float kInt8ScaleFactor = 0x1.04081p-7f;   // fp32((1 + 2^-7) / 127)
+
+template <int FMT>
+__device__ __forceinline__ uint32_t group_scale_bits(float a) {
+  if (FMT == FMT_INT4) {
+    uint32_t t = __float_as_uint(a / 7.0f);
+    constexpr uint32_t kMask = (1u << (24 - 8)) - 1u;
+    if (t & kMask) t = (t | kMask) + 1u;
+    return f32_to_f16_bits(__uint_as_float(t));
+  }
+  return f32_to_f16_bits(__fmul_rn(a, kInt8ScaleFactor));
+}
+
 // Group quantisation of one rotated 128-vector per lane pair (column layout), then
 // packing and storing its codes and scales.  Group g is block b = g.
-//   a = max |r| over the 32 values; s = a / qmax (IEEE fp32 division) rounded up to
-//   8 (INT4) or 4 (INT8) significant bits, stored as fp16;
+//   a = max |r| over the 32 values; s = group_scale_bits<FMT>(a) (fp16);
 //   code = 0 if s == 0, else clamp(rne(r / fp32(s)), -qmax, qmax)
 // INT4 rows are 64 bytes (code 2i in the low nibble of byte i), INT8 rows 128 bytes.
 // `row` points at the vector's code row, `scales` at its 4 fp16 scales; only lanes
@@ -121,7 +141,6 @@ template <int FMT>
 __device__ __forceinline__ void quant_pack_store(const float (&r)[4][16], uint8_t* row,
                                                  uint16_t* scales, bool valid) {
   constexpr float qmax = (FMT == FMT_INT4) ? 7.0f : 127.0f;
-  constexpr int kScaleBits = (FMT == FMT_INT4) ? 8 : 4;   // code bits + scale bits <= 11
   const bool hi = upper_half();
   uint32_t sbits[4];
 #pragma unroll
@@ -130,12 +149,7 @@ __device__ __forceinline__ void quant_pack_store(const float (&r)[4][16], uint8_
 #pragma unroll
     for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(r[b][i]));
     a = fmaxf(a, xor32(a));
-    // scale = a / qmax rounded UP to kScaleBits significant bits (exact in fp16), so
-    // that code * scale is exact in fp16 and the attention kernel dequantises exactly
-    uint32_t t = __float_as_uint(a / qmax);
-    constexpr uint32_t kMask = (1u << (24 - kScaleBits)) - 1u;
-    if (t & kMask) t = (t | kMask) + 1u;
-    sbits[b] = f32_to_f16_bits(__uint_as_float(t));
+    sbits[b] = group_scale_bits<FMT>(a);
     const float s = f16_bits_to_f32(sbits[b]);
     int c[16];
 #pragma unroll

@@ -77,7 +77,6 @@ int launch_packed_attention(const AttnParams& p, void* stream);
 int launch_test_quant_pack(const float* r, int64_t rows, int32_t fmt, void* codes, void* scales,
                            void* stream);
 int launch_test_fwht(const float* in, float* out, int64_t rows, int32_t normalize, void* stream);
-int launch_test_mfma_rate(int32_t dtype, int64_t iters, int64_t n_blocks, float* sink, void* stream);
 const char* hip_error_text(int err);
 
 // Asynchronous copy on `stream` (hipMemcpyAsync); returns a hipError_t value.

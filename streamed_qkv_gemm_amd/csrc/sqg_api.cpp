@@ -35,19 +35,20 @@ int ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Row chunks of `size` over [0, n), last chunk shorter than min_tail folded into the
-// previous one (VRAM Lab page, helpers section, `_ranges`).
+// Row chunks of `size` over [0, n) with a short remainder folded (VRAM Lab page, helpers
+// section, `_ranges`: a last chunk under min_tail rows joins the one before it).  The
+// last chunk starts at the last multiple of `size` below n, or one chunk earlier when
+// fewer than min_tail rows would follow it; every chunk before it is `size` rows.
 std::vector<std::pair<int64_t, int64_t>> chunk_plan(int64_t n, int64_t size, int64_t min_tail) {
   std::vector<std::pair<int64_t, int64_t>> out;
   if (size <= 0 || size >= n) {
     out.emplace_back(0, n);
     return out;
   }
-  for (int64_t a = 0; a < n; a += size) out.emplace_back(a, a + size < n ? a + size : n);
-  if (out.size() > 1 && out.back().second - out.back().first < min_tail) {
-    out.pop_back();
-    out.back().second = n;
-  }
+  int64_t last = ((n - 1) / size) * size;
+  if (last > 0 && n - last < min_tail) last -= size;
+  for (int64_t b = 0; b < last; b += size) out.emplace_back(b, b + size);
+  out.emplace_back(last, n);
   return out;
 }
 
@@ -286,6 +287,22 @@ int attn_prepare(const sqg_attn_args* a, bool check_q, sqg::AttnParams* p, int64
   if (a->qk_mode != SQG_QK_EXACT && a->qk_mode != SQG_QK_FP8)
     return fail(SQG_ERR_INVALID_ARGUMENT, "unknown qk_mode %d", a->qk_mode);
   if (a->reserved != 0) return fail(SQG_ERR_INVALID_ARGUMENT, "attention reserved field not 0");
+  // the kernel reads each (segment, head) block of codes and each head's scale rows
+  // through buffer resources whose byte length is a 32-bit field
+  if (N * 8 > 0x7fffffffLL)
+    return fail(SQG_ERR_UNSUPPORTED, "a head's scales span %lld bytes, more than a 2 GiB buffer resource",
+                (long long)(N * 8));
+  for (int s = 0; s < L.n_segments; ++s) {
+    const int64_t rows = L.seg_end[s] - L.seg_begin[s];
+    for (int h = 0; h < L.n_heads; ++h) {
+      const bool int8 = L.seg_fmt[s] == SQG_INT4_ROT && ((L.seg_int8_heads[s] >> h) & 1ull);
+      const int64_t bytes = rows * (int8 ? 128 : L.seg_row_bytes[s]);
+      if (bytes > 0x7fffffffLL)
+        return fail(SQG_ERR_UNSUPPORTED,
+                    "range %d holds %lld bytes of codes per head, more than a 2 GiB buffer resource",
+                    s, (long long)bytes);
+    }
+  }
   if (N == 0 || q_end == a->q_begin) {
     *empty = true;
     return SQG_OK;
@@ -844,18 +861,6 @@ SQG_API int sqg_test_fwht_f32(const float* in, float* out, int64_t rows, int32_t
   if (!in || !out) return fail(SQG_ERR_INVALID_ARGUMENT, "a device pointer is NULL");
   if (!aligned16(in) || !aligned16(out)) return fail(SQG_ERR_MISALIGNED, "pointers must be 16-byte aligned");
   const int st = launch_status(sqg::launch_test_fwht(in, out, rows, normalize, stream), "test_fwht launch");
-  return st == SQG_OK ? ok() : st;
-}
-
-SQG_API int sqg_test_mfma_rate(int32_t dtype, int64_t iters, int64_t n_blocks, float* sink,
-                               void* stream) {
-  if (dtype != 0 && dtype != 1) return fail(SQG_ERR_INVALID_ARGUMENT, "dtype must be 0 (f16) or 1 (bf16)");
-  if (iters <= 0 || n_blocks <= 0 || n_blocks > 0x7fffffff)
-    return fail(SQG_ERR_INVALID_ARGUMENT, "iters and n_blocks must be positive (n_blocks < 2^31)");
-  if (!sink) return fail(SQG_ERR_INVALID_ARGUMENT, "sink is NULL");
-  if (!aligned16(sink)) return fail(SQG_ERR_MISALIGNED, "sink must be 16-byte aligned");
-  const int st = launch_status(sqg::launch_test_mfma_rate(dtype, iters, n_blocks, sink, stream),
-                               "test_mfma_rate launch");
   return st == SQG_OK ? ok() : st;
 }
 

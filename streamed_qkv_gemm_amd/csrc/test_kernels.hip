@@ -2,9 +2,7 @@
 // the 128-point Hadamard butterfly of device_common.h) on caller-supplied fp32
 // vectors, so that parity tests can check those steps bit for bit in isolation.
 // Each wave takes 32 vectors and holds them in the same column layout the
-// QKV-quant kernel's accumulators have.  A further kernel measures the rate the
-// matrix cores sustain on their own, the ceiling the two product kernels' MFMA
-// utilisation is judged against besides the published peak.
+// QKV-quant kernel's accumulators have.
 #include "device_common.h"
 #include "internal.h"
 
@@ -63,57 +61,7 @@ __global__ __launch_bounds__(64) void test_fwht_kernel(const float* in, float* o
     }
 }
 
-// Matrix cores only: every wave issues `iters` rounds of four independent 32x32x16
-// MFMAs on lane-dependent operands, then stores one sum per thread so that nothing is
-// removed.  2 * 32 * 32 * 16 flop per MFMA.
-template <bool kBf16>
-__global__ __launch_bounds__(256) void test_mfma_rate_kernel(int64_t iters, float* sink) {
-  const int lane = threadIdx.x & 63;
-  f16x8 a, b;
-  bf16x8 ab, bb;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float x = (float)((lane * 8 + i) & 255) * (1.0f / 128.0f) - 1.0f;
-    const float y = (float)((lane * 5 + 3 * i) & 255) * (1.0f / 128.0f) - 1.0f;
-    a[i] = (_Float16)x;
-    b[i] = (_Float16)y;
-    ab[i] = (__bf16)x;
-    bb[i] = (__bf16)y;
-  }
-  f32x16 c[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) c[j][e] = 0.0f;
-  for (int64_t it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (kBf16)
-        c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(j & 1 ? bb : ab, j & 1 ? ab : bb, c[j], 0, 0, 0);
-      else
-        c[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(j & 1 ? b : a, j & 1 ? a : b, c[j], 0, 0, 0);
-    }
-  }
-  float sum = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sum += c[j][e];
-  sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = sum;
-}
-
 }  // namespace
-
-int launch_test_mfma_rate(int32_t dtype, int64_t iters, int64_t n_blocks, float* sink, void* stream) {
-  if (n_blocks <= 0 || iters <= 0) return 0;
-  if (dtype == 1)
-    hipLaunchKernelGGL(test_mfma_rate_kernel<true>, dim3((unsigned)n_blocks), dim3(256), 0,
-                       (hipStream_t)stream, iters, sink);
-  else
-    hipLaunchKernelGGL(test_mfma_rate_kernel<false>, dim3((unsigned)n_blocks), dim3(256), 0,
-                       (hipStream_t)stream, iters, sink);
-  return (int)hipGetLastError();
-}
 
 int launch_test_quant_pack(const float* r, int64_t rows, int32_t fmt, void* codes, void* scales,
                            void* stream) {

@@ -296,11 +296,29 @@ def test_test_entry_argument_errors():
     assert lib.sqg_test_quant_pack_f32(FAKE + 4, 10, 0, FAKE, FAKE, None) == -3
     assert lib.sqg_test_quant_pack_f32(FAKE, 0, 0, None, None, None) == 0
     assert lib.sqg_test_fwht_f32(FAKE, FAKE, -1, 0, None) == -1
-    assert lib.sqg_test_mfma_rate(2, 10, 1, FAKE, None) == -1
-    assert lib.sqg_test_mfma_rate(0, 0, 1, FAKE, None) == -1
-    assert lib.sqg_test_mfma_rate(0, 10, 0, FAKE, None) == -1
-    assert lib.sqg_test_mfma_rate(0, 10, 1, None, None) == -1
-    assert lib.sqg_test_mfma_rate(1, 10, 1, FAKE + 4, None) == -3
+
+
+@pytest.mark.parametrize("n,ranges", [
+    # one head's BF16 codes of an 8,388,736-token range: 256 B x N > 2^31 - 1
+    (8388736, [(0, 8388736, 2)]),
+    # INT8 rows of a masked head inside an INT4 range: 128 B x N > 2^31 - 1
+    (16777344, [(0, 16777344, 0, 1)]),
+    # INT4 rows: 64 B x N > 2^31 - 1
+    (33554560, None),
+    # scales: 8 B x N > 2^31 - 1 for every head, whatever the codes need
+    (268435584, [(0, 128, 0), (128, 268435584, 0)]),
+])
+def test_attention_rejects_stores_beyond_32bit_resources(n, ranges):
+    # the kernel addresses each (range, head) block of codes and each head's scales
+    # through buffer resources with a 32-bit byte length: larger stores are refused
+    # before anything is enqueued
+    lib = sqg.load()
+    arr, nr = B._ranges_array(ranges)
+    a = attn_args(n_tokens=n, d_model=128, n_heads=1, ldq=128, ldo=128,
+                  ranges=ctypes.cast(arr, ctypes.POINTER(B.Range)) if arr is not None else None,
+                  n_ranges=nr)
+    assert lib.sqg_packed_kv_attention(ctypes.byref(a), None) == -2
+    assert b"2 GiB" in lib.sqg_last_error()
 
 
 def test_binding_refuses_cpu_tensors():

@@ -57,8 +57,9 @@ def check_store(lib, x, w, store, segs, layout, okw, rows):
             d_codes = np.abs(codes[integer].astype(np.int64) - ref[t + "_codes"][integer].astype(np.int64))
             assert d_codes.max() <= 1 and np.mean(d_codes == 0) >= 0.999, t
             g, r = scales[integer].astype(np.float64), ref[t + "_scales"][integer].astype(np.float64)
-            sbits = np.where(fm[integer] == INT4, oracle.SCALE_BITS[INT4], oracle.SCALE_BITS[INT8])
-            assert np.all(np.abs(g - r) <= r * 2.0 ** (1 - sbits)[:, None] * 1.0001), t
+            # one step: of the 8-bit INT4 grid, or one fp16 step for INT8
+            rel = np.where(fm[integer] == INT4, 2.0 ** (1 - oracle.INT4_SCALE_BITS), 2.0 ** -10)
+            assert np.all(np.abs(g - r) <= r * rel[:, None] * 1.0001), t
             assert np.mean(g == r) >= 0.98, t
         bf = fm == BF16
         assert np.all(scales[bf] == 0), t

@@ -51,13 +51,13 @@ def fm_rows(n, ranges):
 
 
 def scale_gate(got, want, fmts):
-    """Scales may sit one step apart on their grid (8 significant bits for INT4, 4 for
-    INT8) where the fp32 absmax lands on the other side of a rounding boundary;
-    >= 98% are identical."""
+    """End to end, a scale may sit one step apart where the fp32 absmax lands on the
+    other side of a rounding boundary: one step of the 8-significant-bit grid for INT4,
+    one fp16 step for INT8 (the kvi8r rule rounds to nearest fp16); >= 98% identical."""
     g = got.astype(np.float64)
     w = want.astype(np.float64)
-    bits = np.where(fmts == INT4, oracle.SCALE_BITS[INT4], oracle.SCALE_BITS[INT8])
-    step = w * 2.0 ** (1 - bits)[:, None, None]
+    rel = np.where(fmts == INT4, 2.0 ** (1 - oracle.INT4_SCALE_BITS), 2.0 ** -10)
+    step = w * rel[:, None, None]
     assert np.all(np.abs(g - w) <= step * 1.0001), "scales more than one grid step apart"
     assert np.mean(g == w) >= 0.98
 
@@ -160,15 +160,6 @@ def test_fwht_random_inputs_close(lib):
     assert np.max(np.abs(out - ref)) <= 8 * 2 ** -24 * np.max(np.abs(u)) * math.sqrt(128)
 
 
-def test_mfma_rate_measurement_is_plausible(lib):
-    # the matrix-core-only kernel behind the bench's sustained-rate figure: positive and
-    # below the published dense peak (2.5 PFLOP/s for f16 and bf16)
-    for dtype in (0, 1):
-        r = lib.test_mfma_rate(dtype, iters=2000, repeats=2)
-        assert 50.0 < r < 2600.0, (dtype, r)
-
-
-# ----------------------------------------------------------------------------- projection exactness
 def test_integer_projection_bit_exact_and_chunk_invariant(lib):
     # integer-valued x, W in [-4, 4] at d = 512: all fp32 sums are exact, so Q and,
     # through the exact Hadamard, every K/V code and scale match the oracle bit for bit

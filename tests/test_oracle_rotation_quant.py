@@ -81,15 +81,31 @@ def brute_force_codes(r_group, s16, qmax):
     return np.array(out)
 
 
-def scale_by_definition(a, qmax, bits):
-    """Smallest number with `bits` significant bits that is >= fp32(a / qmax), as fp16
-    (float64 arithmetic on exponent and step, independent of the bit-pattern code)."""
-    t = float(np.float32(np.float32(a) / np.float32(qmax)))
+def scale_by_definition(a, qmax):
+    """The group scale computed from the two rules' statements, independently of the
+    oracle's bit-pattern code:
+      INT4: the smallest number with 8 significant bits that is >= fp32(a / 7), as fp16
+            (float64 arithmetic on exponent and step);
+      INT8: the fp16 value nearest to t = fp32(a * fp32((1 + 2^-7) / 127)), ties to an
+            even significand, found by scanning the fp16 grid around t ([VL] kvi8r
+            `_Int8KV.store`)."""
+    if qmax == QMAX[INT4]:
+        t = float(np.float32(np.float32(a) / np.float32(qmax)))
+        if t == 0.0:
+            return np.float16(0.0)
+        e = math.floor(math.log2(t))
+        step = 2.0 ** (e - 8 + 1)
+        return np.float16(math.ceil(t / step) * step)
+    c8 = np.float32(129.0 / (127.0 * 128.0))
+    t = float(np.float32(np.float32(a) * c8))
     if t == 0.0:
         return np.float16(0.0)
-    e = math.floor(math.log2(t))
-    step = 2.0 ** (e - bits + 1)
-    return np.float16(math.ceil(t / step) * step)
+    e = max(math.floor(math.log2(t)), -14)        # fp16 binade (subnormals share -14)
+    step = 2.0 ** (e - 10)
+    lo = math.floor(t / step) * step
+    cands = [lo, lo + step]
+    best = min(cands, key=lambda v: (abs(v - t), (int(round(v / step)) & 1)))
+    return np.float16(best)
 
 
 def test_round_up_bits_examples():
@@ -100,13 +116,47 @@ def test_round_up_bits_examples():
     assert oracle.round_up_bits(np.float32(1.0625), 4) == 1.125
 
 
-@pytest.mark.parametrize("fmt", [INT4, INT8])
-def test_code_times_scale_exact_in_fp16(fmt):
-    rng = np.random.default_rng(8 + fmt)
+def test_int8_scale_factor_is_the_pages_constant():
+    # [VL] kvi8r `_Int8KV.store`: absmax * (1/127) * (1 + 2^-7), i.e. 129 / 16256, as the
+    # fp32 value the page's fp32 tensor is multiplied by
+    exact = 129.0 / 16256.0
+    assert abs(float(oracle.INT8_SCALE_FACTOR) - exact) <= 2.0 ** -24 * exact
+    assert oracle.INT8_SCALE_FACTOR.dtype == np.float32
+
+
+def test_int8_worked_example_group_max_127():
+    # A group whose largest magnitude is 127: the scale is 127 * 129/16256 = 1.0078125
+    # (exact in fp16), so the largest element maps to round(127 / 1.0078125) = 126, not
+    # 127 -- the enlargement keeps the row maximum inside the code range.  Dropping the
+    # factor would give scale 1 and code 127.
+    r = np.zeros((1, 128), np.float32)
+    r[0, :32] = np.linspace(-127.0, 127.0, 32, dtype=np.float32)
+    codes, scales = oracle.quantize_groups(r, QMAX[INT8])
+    assert float(scales[0, 0]) == 1.0078125
+    assert codes[0, 0] == -126 and codes[0, 31] == 126
+    assert float(scales[0, 1]) == 0.0 and np.all(codes[0, 32:] == 0)
+
+
+def test_int4_scale_keeps_8_bits_and_code_times_scale_is_exact_in_fp16():
+    rng = np.random.default_rng(8)
     r = (rng.standard_normal((500, 128)) * rng.uniform(0.01, 50, size=(500, 1))).astype(np.float32)
-    codes, scales = oracle.quantize_groups(r, QMAX[fmt])
+    codes, scales = oracle.quantize_groups(r, QMAX[INT4])
     prod = codes.reshape(500, 4, 32).astype(np.float64) * scales.astype(np.float64)[..., None]
     assert np.array_equal(prod.astype(np.float16).astype(np.float64), prod)
+
+
+def test_int8_scale_within_the_pages_factor():
+    # fp32 product then fp16 rounding: s / (a / 127) lies within one fp16 half-step of
+    # the page's factor (1 + 2^-7) for normal fp16 scales, so |r / s| < 127 always
+    rng = np.random.default_rng(9)
+    r = (rng.standard_normal((2000, 128)) * rng.uniform(0.05, 50, size=(2000, 1))).astype(np.float32)
+    codes, scales = oracle.quantize_groups(r, QMAX[INT8])
+    a = np.max(np.abs(r.reshape(2000, 4, 32)), axis=-1).astype(np.float64)
+    ratio = scales.astype(np.float64) / (a / 127.0)
+    f = 1.0 + 2.0 ** -7
+    assert np.all(ratio >= f * (1 - 2.0 ** -11) * (1 - 2.0 ** -23))
+    assert np.all(ratio <= f * (1 + 2.0 ** -11) * (1 + 2.0 ** -23))
+    assert np.all(np.abs(codes.astype(np.int64)) <= 127)
 
 
 @pytest.mark.parametrize("fmt", [INT4, INT8])
@@ -114,14 +164,15 @@ def test_quantizer_matches_brute_force(fmt):
     qmax = QMAX[fmt]
     rng = np.random.default_rng(3 + fmt)
     r = (rng.standard_normal((6, 128)) * rng.uniform(0.01, 5, size=(6, 1))).astype(np.float32)
+    r[5] *= 1e-4                                    # small scales (subnormal fp16 for INT8)
     codes, scales = oracle.quantize_groups(r, qmax)
     assert codes.dtype == np.int8 and scales.dtype == np.float16
     for row in range(r.shape[0]):
         for g in range(4):
             grp = r[row, 32 * g:32 * g + 32]
             a = float(np.max(np.abs(grp)))
-            s16 = scale_by_definition(a, qmax, oracle.SCALE_BITS[fmt])
-            assert scales[row, g] == s16
+            s16 = scale_by_definition(a, qmax)
+            assert scales[row, g] == s16, (fmt, row, g, float(scales[row, g]), float(s16))
             assert np.array_equal(codes[row, 32 * g:32 * g + 32], brute_force_codes(grp, s16, qmax))
 
 
@@ -140,17 +191,43 @@ def test_dequant_error_at_most_half_scale(fmt):
 def test_absmax_element_maps_to_qmax():
     rng = np.random.default_rng(6)
     r = (rng.standard_normal((64, 128))).astype(np.float32)
-    for fmt in (INT4, INT8):
+    for fmt, lo in ((INT4, 7), (INT8, 126)):
         codes, _ = oracle.quantize_groups(r, QMAX[fmt])
         g = r.reshape(64, 4, 32)
         c = codes.reshape(64, 4, 32)
         idx = np.argmax(np.abs(g), axis=-1)
         top = np.take_along_axis(c, idx[..., None], -1)[..., 0]
-        # the scale is at most a factor (1 + 2^(1 - bits)) above absmax/qmax
-        lo = math.ceil(QMAX[fmt] / (1 + 2.0 ** (1 - oracle.SCALE_BITS[fmt])) - 0.5)
+        # INT4: the 8-bit round-up moves a / s by less than 2^-7, so the top code is 7;
+        # INT8: the page's (1 + 2^-7) enlargement puts the top element at 126 or 127
         assert np.all(np.abs(top) <= QMAX[fmt]) and np.all(np.abs(top) >= lo)
-        if fmt == INT4:
-            assert np.all(np.abs(top) == 7)
+
+
+def test_quantisation_error_of_each_scale_rule_against_unquantised_rows():
+    # rms error of the dequantised rows against the unquantised rotated rows, for the
+    # rules in the oracle and two alternatives: the unrounded scale a / qmax (the floor
+    # any fp16 rule sits on) and, for INT8, a scale grid of 4 significant bits.  The
+    # page's INT8 rule stays within 1% of the floor; a 4-bit grid costs >= 4% more.
+    rng = np.random.default_rng(12)
+    u = rng.standard_normal((20000, 128))
+    r = oracle.rotate(u)
+    g = r.reshape(-1, 4, 32).astype(np.float64)
+    a = np.max(np.abs(g), axis=-1)
+
+    def rms(scale, qmax):
+        s = np.where(scale == 0, 1.0, scale)[..., None]
+        c = np.clip(np.rint(g / s), -qmax, qmax)
+        return float(np.sqrt(np.mean((c * s - g) ** 2)))
+
+    for fmt in (INT4, INT8):
+        qmax = QMAX[fmt]
+        codes, scales = oracle.quantize_groups(r, qmax)
+        err = float(np.sqrt(np.mean((oracle.dequantize(codes, scales) - r.astype(np.float64)) ** 2)))
+        floor = rms(a / qmax, qmax)
+        assert floor <= err <= 1.01 * floor, (fmt, err, floor)
+    grid4 = oracle.round_up_bits((a / 127.0).astype(np.float32), 4).astype(np.float16).astype(np.float64)
+    codes, scales = oracle.quantize_groups(r, 127)
+    page = float(np.sqrt(np.mean((oracle.dequantize(codes, scales) - r.astype(np.float64)) ** 2)))
+    assert rms(grid4, 127) >= 1.04 * page
 
 
 def test_one_hot_vector_codes_follow_hadamard_signs():
@@ -163,7 +240,7 @@ def test_one_hot_vector_codes_follow_hadamard_signs():
         r = oracle.rotate(e)
         codes, scales = oracle.quantize_groups(r, 7)
         assert np.array_equal(codes[0], 7 * H[j])
-        expect = scale_by_definition(np.float32(1 / math.sqrt(128)), 7, 8)
+        expect = scale_by_definition(np.float32(1 / math.sqrt(128)), 7)
         assert np.all(scales == expect)
 
 
