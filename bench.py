@@ -271,11 +271,6 @@ def main():
             bf16_base = {"error": str(exc)[:200]}
         torch.cuda.empty_cache()
 
-    # ---- the rate the matrix cores sustain on this device under a pure MFMA load (a
-    # kernel of independent 32x32x16 MFMAs only): the practical ceiling beside the
-    # published peak
-    sustained = {"f16": sqg.test_mfma_rate(0, device=dev), "bf16": sqg.test_mfma_rate(1, device=dev)}
-
     result = {
         "metric": METRIC,
         "value": (qkv_flop + att_flop) / (step_ms * 1e-3) / 1e12,
@@ -323,14 +318,11 @@ def main():
             "algorithmic_flop_per_step": att_flop,
             # the split query runs QK^T as two f16 MFMAs: executed MFMA flop = 1.5 x algorithmic
             "executed_mfma_flop_factor": 1.5,
-            "sustained_mfma_tflops": sustained["f16"],
-            "frac_of_sustained": att_tflops / sustained["f16"],
         },
         "qkv_roofline": {
             "kernel": "qkv_quant_kernel", "bound": "mfma", "achieved": qkv_tflops,
             "peak": PEAK_TFLOPS_F16, "unit": "TFLOP/s", "frac": qkv_tflops / PEAK_TFLOPS_F16,
             "launches_per_step": n_chunks, "avg_launch_ms": qkv_ms / n_chunks,
-            "sustained_mfma_tflops": sustained["bf16"], "frac_of_sustained": qkv_tflops / sustained["bf16"],
         },
     }
 

@@ -127,7 +127,12 @@ __device__ __forceinline__ uint32_t group_scale_bits(float a) {
     if (t & kMask) t = (t | kMask) + 1u;
     return f32_to_f16_bits(__uint_as_float(t));
   }
-  return f32_to_f16_bits(__fmul_rn(a, kInt8ScaleFactor));
+  // the product is rounded to fp32 first: the barrier keeps the compiler from fusing
+  // multiply and conversion into one mixed-precision FMA, which rounds once (to f16)
+  // and differs from the rule where the fp32 rounding moves a value across an f16 tie
+  float t = __fmul_rn(a, kInt8ScaleFactor);
+  asm volatile("" : "+v"(t));
+  return f32_to_f16_bits(t);
 }
 
 // Group quantisation of one rotated 128-vector per lane pair (column layout), then

@@ -10,11 +10,17 @@
 // online softmax, and the output is rotated back once.  That page also measured
 // that the rotated basis needs fp16 operands rather than bf16 (rotation spreads
 // every value to the same magnitude), so both products use f16 MFMA with fp32
-// accumulation.  Two further steps keep the scores accurate where softmax is
-// sharp: K/V dequantise exactly (the store's scales carry few enough bits that
-// code * scale is an fp16 value), and the rotated query is split into an f16 high
-// part and an f16 remainder, so S = K (q_hi + q_lo) costs two MFMAs per step and
-// carries ~22 bits of the query.
+// accumulation.  Where softmax is sharp the scores need more than the 11 bits an
+// f16 query carries, so the rotated query is split into an f16 high part and a
+// remainder (about 2^-12 of it), and the scores are
+//   S = K_f16 q_hi  (f16 MFMA)  +  K_6 q_lo6  (block-scaled fp6 MFMA)
+// with K_6 and q_lo6 the keys and the remainder in fp6 E2M3 with one E8M0 exponent
+// per group of 32 dims (the store's quantisation groups).  The fp6 product runs at
+// four times the f16 rate and carries the remainder to ~2^-4, so the scores keep
+// ~16 bits for 1/8 more matrix work instead of 1/2.  INT4 keys are exact in f16 (the
+// store's INT4 scales have 8 significant bits); INT8 keys are not (kvi8r scales are
+// full fp16), so INT8 tiles add K_lo q_hi with K_lo = code * scale - f16(code * scale),
+// exact in f16.
 //
 // Workgroup: 256 queries of one head, eight waves of 32 queries (two waves per
 // SIMD, so one wave's softmax and dequantisation overlap the other's MFMAs).
@@ -105,6 +111,45 @@ __device__ __forceinline__ void dequant_int8x4(uint32_t w, uint32_t s2, uint32_t
   }
 }
 
+// The remainders code * scale - f16(code * scale) of 4 INT8 codes (one dword, code j in
+// byte j), as 4 f16 values: code * scale has at most 7 + 11 significant bits, so it is
+// exact in fp32 and its remainder after the f16 rounding is exact in f16 (outside the
+// f16 subnormal range)
+__device__ __forceinline__ void dequant_int8x4_rem(uint32_t w, uint32_t s2, uint32_t (&out)[2]) {
+  const uint32_t b = w ^ 0x80808080u;
+  const f16x2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  const f16x2 sc = __builtin_bit_cast(f16x2, s2);
+  const float sf = (float)sc[0];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const uint32_t sel = (uint32_t)(2 * p) | 0x0c00u | ((uint32_t)(2 * p + 1) << 16) | 0x0c000000u;
+    const uint32_t pr = __builtin_amdgcn_perm(0u, b, sel) | 0x64006400u;
+    const f16x2 c = __builtin_bit_cast(f16x2, pr) + bias;   // exact codes
+    const f16x2 v = c * sc;                                  // as stored in the K tile
+    const f16x2 r = {(_Float16)((float)c[0] * sf - (float)v[0]), (_Float16)((float)c[1] * sf - (float)v[1])};
+    out[p] = __builtin_bit_cast(uint32_t, r);
+  }
+}
+
+// E8M0 exponent for fp6 E2M3 values (largest magnitude 7.5): the smallest e with
+// a <= 7.5 * 2^e for a finite a >= 0 (a = 1.m * 2^E: e = E - 2 if 1.m <= 1.875, else
+// E - 1), clamped to [-126, 127] so that 2^e is a normal fp32 scale.
+__device__ __forceinline__ int fp6_exponent(float a) {
+  const uint32_t b = __float_as_uint(a);
+  const int e = (int)(b >> 23) - 129 + ((b & 0x7fffffu) > 0x700000u ? 1 : 0);
+  return e < -126 ? -126 : (e > 127 ? 127 : e);
+}
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
+typedef _Float16 f16x32 __attribute__((ext_vector_type(32)));
+typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
+
+// 32 f16 values as fp6 E2M3 codes of value / 2^e (round to nearest even, value i in
+// bits 6i .. 6i + 5 of the six dwords)
+__device__ __forceinline__ u32x6 to_fp6(const f16x32 v, int e) {
+  return __builtin_amdgcn_cvt_scalef32_pk32_fp6_f16(v, pow2f(e));
+}
+
 // Packed codes and the group scale one thread moves per tile: 32 values of one key
 // (16 B INT4 in c0, 32 B INT8 in c0, c1); BF16 tiles are read later, in store_tile,
 // from the tile's byte offset crow.
@@ -132,13 +177,22 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 // a lane's 16-byte halves of a 64-dim chunk are the dims the scaled MFMA pairs with
 // the query bytes held in registers (see the QK^T step)
 constexpr int kK8Stride = 128 + 16;
+// fp6 K rows in LDS: the four groups of one key, 24 bytes each (32 E2M3 codes in
+// dim order), then 8 bytes of padding: consecutive keys start 13 eight-byte slots
+// apart, so the 32 keys of one 8-byte operand read fall in distinct bank pairs.
+constexpr int kK6Stride = 104;
 
 template <bool kFp8QK>
 __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(16))) _Float16 sK[2][kKTile];
   __shared__ __attribute__((aligned(16))) _Float16 sV[2][kVTile];
-  __shared__ __attribute__((aligned(16))) _Float16 sQl[kFp8QK ? 1 : kWaves][32 * kHeadDim];
-  __shared__ uint32_t sKe[2][kBKV];   // fp8 QK: the four E8M0 exponents of each key (byte g)
+  // exact tier: the keys as fp6 for the remainder term, and the f16 remainders of INT8 keys
+  __shared__ __attribute__((aligned(16))) uint8_t sK6[kFp8QK ? 1 : 2][kFp8QK ? 16 : kBKV * kK6Stride];
+  __shared__ __attribute__((aligned(16))) _Float16 sKlo[kFp8QK ? 1 : 2][kFp8QK ? 8 : kKTile];
+  // exact tier: each wave's fp6 query remainder, [chunk][lane][6 dwords]
+  __shared__ __attribute__((aligned(16))) uint32_t sQ6[kFp8QK ? 1 : kWaves][kFp8QK ? 2 : 2 * 64 * 6];
+  __shared__ uint32_t sKe[2][kBKV];   // the four E8M0 exponents of each key (byte g = group g)
+  __shared__ int32_t sKfmt[2];        // format of the K tile in each stage
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -152,9 +206,9 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
   // or (fp8 QK) E4M3 codes with one E8M0 exponent per group of 32 dims
   const int64_t qrow = p.q_begin + (int64_t)blockIdx.x * kBQ + 32 * wave + l32;
   const bool qvalid = qrow < p.q_end;
-  f16x8 qf[8], ql[8];
-  i32x8 q8[2];
-  uint32_t q8e[2];
+  f16x8 qf[8];
+  i32x8 q8[2];        // fp8 tier: the E4M3 query (the exact tier keeps its fp6 remainder in LDS)
+  uint32_t q8e[2];    // the E8M0 exponent byte this lane supplies for each 64-dim chunk
   {
     const uint16_t* src = p.q + ((qvalid ? qrow : p.q_begin) - p.q_row0) * p.ldq + head * kHeadDim + 8 * hsel;
     // element e(ks, j) = 16 ks + 8 hsel + j: bits 0-2 = j, bit 3 = lane pair, bits 4-6 = ks.
@@ -249,6 +303,7 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
         }
     }
     if constexpr (!kFp8QK) {
+      f16x8 ql[8];
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
@@ -257,9 +312,42 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
           qf[ks][j] = hi;
           ql[ks][j] = (_Float16)(v[ks][j] - (float)hi);
         }
+      // fp6 operand of the remainder: for chunk c (dims 64 c .. + 63) this lane supplies
+      // group 2 c + hsel whole, 32 values in dim order.  It holds the half of that group
+      // with dim bit 3 = hsel; the partner lane sends the other half.
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        *reinterpret_cast<f16x8*>(&sQl[wave][(ks * 64 + lane) * 8]) = ql[ks];
+      for (int c = 0; c < 2; ++c) {
+        f16x8 got[2];   // the partner's half of this lane's group, k-steps 4 c + 2 hsel + t
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const u32x4 snd = __builtin_bit_cast(u32x4, hsel ? ql[4 * c + t] : ql[4 * c + 2 + t]);
+          u32x4 rcv;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) rcv[k] = xor32u(snd[k]);
+          got[t] = __builtin_bit_cast(f16x8, rcv);
+        }
+        f16x32 g;
+        float amax = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const f16x8 mine = hsel ? ql[4 * c + 2 + t] : ql[4 * c + t];
+          const f16x8 lo8 = hsel ? got[t] : mine;   // dims 16 t + 0 .. 7 of the group
+          const f16x8 hi8 = hsel ? mine : got[t];   // dims 16 t + 8 .. 15
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            g[16 * t + j] = lo8[j];
+            g[16 * t + 8 + j] = hi8[j];
+            amax = fmaxf(amax, fmaxf(fabsf((float)lo8[j]), fabsf((float)hi8[j])));
+          }
+        }
+        const int e = fp6_exponent(amax);
+        const u32x6 w6 = to_fp6(g, e);
+        u32x2* q6 = reinterpret_cast<u32x2*>(&sQ6[wave][(c * 64 + lane) * 6]);
+        q6[0] = u32x2{w6[0], w6[1]};
+        q6[1] = u32x2{w6[2], w6[3]};
+        q6[2] = u32x2{w6[4], w6[5]};
+        q8e[c] = (uint32_t)(e + 127);
+      }
     } else {
       // group g = dims 32 g .. + 31 = k-steps 2 g, 2 g + 1 of both lanes of the pair
       int eg[4];
@@ -288,7 +376,6 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
       }
     }
   }
-  const _Float16* qlw = sQl[kFp8QK ? 0 : wave];
 
   // ---- per-thread maps for the K/V tile loads (64 keys per tile, 512 threads): waves
   // 0-3 bring K, waves 4-7 bring V; thread (key, grp) moves group grp (32 values) of one
@@ -343,6 +430,7 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
     _Float16* dst = (vside ? sV[stage] : sK[stage]) + tkey * kKStride + 32 * tgrp;
     const int fmt = __builtin_amdgcn_readfirstlane(r.fmt);
     const uint32_t s2 = r.scale | (r.scale << 16);
+    constexpr bool kSplit = !kFp8QK;   // exact tier: INT8 keys carry their f16 remainder
     uint32_t o[16];
     if (fmt == FMT_INT4) {
 #pragma unroll
@@ -372,20 +460,45 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
     }
     if (kFp8QK && !vside) {
       // K as E4M3 codes of value / 2^e with e the group's E8M0 exponent; bytes of dims
-      // 8..15 and 16..23 of the group trade places (the swap of dim bits 3 and 4)
-      f16x2 m2 = {(_Float16)0.0f, (_Float16)0.0f};
-#pragma unroll
-      for (int i = 0; i < 16; ++i) m2 = __builtin_elementwise_max(m2, __builtin_elementwise_abs(__builtin_bit_cast(f16x2, o[i])));
-      const float a = fmaxf((float)m2[0], (float)m2[1]);
-      const int e = e8m0_exponent(a);
-      const float sc = a > 0.0f ? ldexpf(1.0f, e) : 1.0f;
+      // 8..15 and 16..23 of the group trade places (the swap of dim bits 3 and 4).  The
+      // codes are taken from the exact decoded value: INT4 and BF16 keys are exact in
+      // f16, INT8 keys (code * scale, up to 18 significant bits) are formed in fp32.
       uint32_t w[8];
+      int e;
+      if (fmt != FMT_INT8) {
+        f16x2 m2 = {(_Float16)0.0f, (_Float16)0.0f};
 #pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const s16x2 zero = {0, 0};
-        s16x2 r2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(zero, __builtin_bit_cast(f16x2, o[2 * d]), sc, false);
-        r2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r2, __builtin_bit_cast(f16x2, o[2 * d + 1]), sc, true);
-        w[d] = __builtin_bit_cast(uint32_t, r2);
+        for (int i = 0; i < 16; ++i) m2 = __builtin_elementwise_max(m2, __builtin_elementwise_abs(__builtin_bit_cast(f16x2, o[i])));
+        const float a = fmaxf((float)m2[0], (float)m2[1]);
+        e = e8m0_exponent(a);
+        const float sc = a > 0.0f ? ldexpf(1.0f, e) : 1.0f;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          const s16x2 zero = {0, 0};
+          s16x2 r2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(zero, __builtin_bit_cast(f16x2, o[2 * d]), sc, false);
+          r2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r2, __builtin_bit_cast(f16x2, o[2 * d + 1]), sc, true);
+          w[d] = __builtin_bit_cast(uint32_t, r2);
+        }
+      } else {
+        const float sf = f16_bits_to_f32(r.scale & 0xffffu);
+        float a = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t cw = q < 4 ? r.c0[q] : r.c1[q - 4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) a = fmaxf(a, fabsf((float)(int8_t)(cw >> (8 * j)) * sf));
+        }
+        e = e8m0_exponent(a);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t cw = q < 4 ? r.c0[q] : r.c1[q - 4];
+          float v[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = ldexpf((float)(int8_t)(cw >> (8 * j)) * sf, -e);
+          int x = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+          x = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], x, true);
+          w[q] = (uint32_t)x;
+        }
       }
       uint8_t* k8 = reinterpret_cast<uint8_t*>(sK[stage]) + tkey * kK8Stride + 32 * tgrp;
       const u32x4 lo = {w[0], w[1], w[4], w[5]};
@@ -405,6 +518,46 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
       for (int i = 0; i < 4; ++i) {
         const u32x4 v = {o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
         *reinterpret_cast<u32x4*>(dst + 8 * i) = v;
+      }
+      if constexpr (kSplit) {
+        // the group as fp6 for the remainder term; its exponent covers the group's
+        // largest magnitude: 7 s (INT4) or 127 s (INT8) from the scale, else the values
+        float amax;
+        if (fmt == FMT_BF16) {
+          f16x2 m2 = {(_Float16)0.0f, (_Float16)0.0f};
+#pragma unroll
+          for (int i = 0; i < 16; ++i) m2 = __builtin_elementwise_max(m2, __builtin_elementwise_abs(__builtin_bit_cast(f16x2, o[i])));
+          amax = fmaxf((float)m2[0], (float)m2[1]);
+        } else {
+          amax = f16_bits_to_f32(r.scale & 0xffffu) * (fmt == FMT_INT4 ? 7.0f : 127.0f);
+        }
+        const int e = fp6_exponent(amax);
+        f16x32 g;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const f16x2 h = __builtin_bit_cast(f16x2, o[i]);
+          g[2 * i] = h[0];
+          g[2 * i + 1] = h[1];
+        }
+        const u32x6 w6 = to_fp6(g, e);
+        u32x2* k6 = reinterpret_cast<u32x2*>(sK6[stage] + tkey * kK6Stride + 24 * tgrp);
+        k6[0] = u32x2{w6[0], w6[1]};
+        k6[1] = u32x2{w6[2], w6[3]};
+        k6[2] = u32x2{w6[4], w6[5]};
+        reinterpret_cast<uint8_t*>(sKe[stage])[4 * tkey + tgrp] = (uint8_t)(e + 127);
+        if (fmt == FMT_INT8) {
+          // second pass over the codes: the f16 remainders of the INT8 keys
+          _Float16* lrow = sKlo[stage] + tkey * kKStride + 32 * tgrp;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint32_t a[2], b[2];
+            dequant_int8x4_rem(i < 2 ? r.c0[2 * i] : r.c1[2 * i - 4], s2, a);
+            dequant_int8x4_rem(i < 2 ? r.c0[2 * i + 1] : r.c1[2 * i - 3], s2, b);
+            const u32x4 v = {a[0], a[1], b[0], b[1]};
+            *reinterpret_cast<u32x4*>(lrow + 8 * i) = v;
+          }
+        }
+        if (tid == 0) sKfmt[stage] = fmt;
       }
     }
   };
@@ -439,15 +592,43 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
 
   auto do_qk = [&](int stage, f32x16 (&s)[kKB]) {
     const _Float16* K = sK[stage];
+    // remainder term: per 32-key block and 64-dim chunk one block-scaled fp6 MFMA; lane
+    // (key, hsel) supplies group 2 c + hsel of its key and that group's exponent
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) {
+      const uint32_t ew = sKe[stage][32 * kb + l32];
+      const uint8_t* row = sK6[stage] + (32 * kb + l32) * kK6Stride + 24 * hsel;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const u32x2 a0 = *reinterpret_cast<const u32x2*>(row + 48 * c);
+        const u32x2 a1 = *reinterpret_cast<const u32x2*>(row + 48 * c + 8);
+        const u32x2 a2 = *reinterpret_cast<const u32x2*>(row + 48 * c + 16);
+        const i32x8 A = {(int)a0[0], (int)a0[1], (int)a1[0], (int)a1[1], (int)a2[0], (int)a2[1], 0, 0};
+        const u32x2* q6 = reinterpret_cast<const u32x2*>(&sQ6[kFp8QK ? 0 : wave][(c * 64 + lane) * 6]);
+        const u32x2 b0 = q6[0], b1 = q6[1], b2 = q6[2];
+        const i32x8 B = {(int)b0[0], (int)b0[1], (int)b1[0], (int)b1[1], (int)b2[0], (int)b2[1], 0, 0};
+        const int ea = (int)((ew >> (8 * (2 * c + hsel))) & 0xffu);
+        const f32x16 acc = c == 0 ? f32x16{} : s[kb];
+        s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc, 2, 2, 0, ea, 0, (int)q8e[c]);
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const f16x8 lo = *reinterpret_cast<const f16x8*>(qlw + (ks * 64 + lane) * 8);
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb) {
         const f16x8 kf = *reinterpret_cast<const f16x8*>(K + (32 * kb + l32) * kKStride + 16 * ks + 8 * hsel);
-        const f32x16 acc = ks == 0 ? f32x16{} : s[kb];
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], acc, 0, 0, 0);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, lo, s[kb], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], s[kb], 0, 0, 0);
+      }
+    }
+    if (__builtin_amdgcn_readfirstlane(sKfmt[stage]) == FMT_INT8) {
+      const _Float16* Kl = sKlo[stage];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb) {
+          const f16x8 kf = *reinterpret_cast<const f16x8*>(Kl + (32 * kb + l32) * kKStride + 16 * ks + 8 * hsel);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], s[kb], 0, 0, 0);
+        }
       }
     }
   };

@@ -428,19 +428,20 @@ int qkv_prepare(const sqg_qkv_args* a, bool check_store, sqg::QkvParams* pp, sqg
   return SQG_OK;
 }
 
-// One attention pass of p's query rows over keys [kv_begin, kv_end), in key blocks of
-// kv_block rows merged through the LSE buffer (the first block honours `accumulate`).
-int attn_launch_blocks(sqg::AttnParams p, int64_t kv_begin, int64_t kv_end, int64_t kv_block,
-                       int32_t accumulate, void* stream) {
-  const auto blocks = chunk_plan(kv_end - kv_begin, kv_block, 512);
-  for (size_t i = 0; i < blocks.size(); ++i) {
-    p.kv_begin = kv_begin + blocks[i].first;
-    p.kv_end = kv_begin + blocks[i].second;
-    p.accumulate = (i == 0) ? accumulate : 1;
-    const int st = launch_status(sqg::launch_packed_attention(p, stream), "packed_kv_attention launch");
-    if (st != SQG_OK) return st;
-  }
-  return SQG_OK;
+// One attention pass of p's query rows over keys [kv_begin, kv_end) (`accumulate` merges
+// into the (O, LSE) already in the buffers), as one launch whatever kv_block is.  The
+// kernel walks the key range tile by tile keeping the running maximum, sum and
+// unnormalised O of each query in registers; merging a block's partial (o_b, lse_b)
+// into (o, lse) by the log-sum-exp rule of VRAM Lab's `_online_combine` gives exactly
+// what continuing that running state over the block's keys gives (both are
+// sum_j e^(s_j) v_j / sum_j e^(s_j) over the keys so far), so the KV blocks are merged
+// in registers as the walk crosses them, and O, LSE and Q are read and written once.
+int attn_launch_blocks(sqg::AttnParams p, int64_t kv_begin, int64_t kv_end, int32_t accumulate,
+                       void* stream) {
+  p.kv_begin = kv_begin;
+  p.kv_end = kv_end;
+  p.accumulate = accumulate;
+  return launch_status(sqg::launch_packed_attention(p, stream), "packed_kv_attention launch");
 }
 
 // Default query chunk of the Q-recompute mode: 16384 rows, or more when there are few
@@ -591,7 +592,7 @@ SQG_API int sqg_packed_kv_attention(const sqg_attn_args* a, void* stream) {
   int st = attn_prepare(a, true, &p, &kv_end, &empty);
   if (st != SQG_OK) return st;
   if (empty) return ok();
-  st = attn_launch_blocks(p, a->kv_begin, kv_end, a->kv_block, a->accumulate, stream);
+  st = attn_launch_blocks(p, a->kv_begin, kv_end, a->accumulate, stream);
   return st == SQG_OK ? ok() : st;
 }
 
@@ -681,7 +682,7 @@ SQG_API int sqg_packed_kv_attention_qrecompute(const sqg_qrecompute_args* a, voi
     cp.q_begin = c0;
     cp.q_end = c1;
     cp.q_row0 = c0;
-    st = attn_launch_blocks(cp, at.kv_begin, kv_end, at.kv_block, at.accumulate, stream);
+    st = attn_launch_blocks(cp, at.kv_begin, kv_end, at.accumulate, stream);
     if (st != SQG_OK) return st;
   }
   return ok();

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import synth
-from test_gpu_parity import q_gate
+from test_gpu_parity import q_gate, scale_gate
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -56,17 +56,20 @@ def test_fullsize_parity(lib, name):
     layout, _ = oracle.packed_layout(N, H, segs)
     kp, vp = host(store["kpack"]), host(store["vpack"])
     ks, vs = host(store["kscale"]), host(store["vscale"])
-    kc, _ = oracle.gather_packed_rows(kp, ks, layout, H, rows)
-    vc, _ = oracle.gather_packed_rows(vp, vs, layout, H, rows)
+    kc, ksc = oracle.gather_packed_rows(kp, ks, layout, H, rows)
+    vc, vsc = oracle.gather_packed_rows(vp, vs, layout, H, rows)
     qb = synth.bf16_bits(store["q"])
     for got, want in ((kc, ref["k_codes"]), (vc, ref["v_codes"])):
         dd = np.abs(got.astype(np.int64) - want.astype(np.int64))
         assert dd.max() <= 1 and np.mean(dd == 0) >= 0.999, (name, dd.max(), np.mean(dd == 0))
+    scale_gate(ksc, ref["k_scales"], fm)
+    scale_gate(vsc, ref["v_scales"], fm)
     q_gate(qb[rows], ref["q_bits"], name)
 
-    # ---- G3 on sampled query rows of a few heads, all keys
-    qrows = synth.sample_rows(N, 12, seed=wl.seed_base + 6, must=[N - 1]).numpy()
-    heads = [0, H // 2, H - 1]
+    # ---- G3 on 32 sampled query rows (the last row and, with a policy, both sides of
+    # every range boundary among them) x 8 heads spread over the head range, all keys
+    qrows = synth.sample_rows(N, 32, seed=wl.seed_base + 6, must=[N - 1] + extra).numpy()
+    heads = sorted(set(np.linspace(0, H - 1, 8).round().astype(int).tolist()))
     o_ref, lse_ref = oracle.attention_rows_from_store(qb[qrows], qrows, kp, vp, ks, vs, layout, H, N,
                                                       kv_block=wl.kv_block, heads=heads)
     og = host(o)[qrows]
@@ -120,9 +123,20 @@ def test_fullsize_variants_217k(lib):
     assert torch.equal(o1[qr], o_ref) and torch.equal(l1[:, qr], l_ref)
     del o1, l1, kv
     torch.cuda.empty_cache()
-    # host-staged K/V in blocks of the KV-block size
+    # host-staged K/V in blocks of the KV-block size: one launch per block merged through
+    # the LSE, against the device path's single walk over the blocks (equal up to
+    # rounding), and on its own against the oracle
     st = lib.alloc_staged(N, d, wl.kv_block, wl.ranges, device=DEV)
     lib.streamed_qkv_quant_staged(x, w, st, emit=lib.SQG_EMIT_KV, **kw)
     o2, l2 = lib.packed_kv_attention_staged(st, store["q"])
     torch.cuda.synchronize()
-    assert torch.equal(o2[qr], o_ref) and torch.equal(l2[:, qr], l_ref)
+    assert float((o2[qr] - o_ref).abs().max()) <= 2e-3 and float((l2[:, qr] - l_ref).abs().max()) <= 1e-4
+    want, lse_want = oracle.attention_rows_from_store(qb[qrows], qrows, *args, kv_block=wl.kv_block,
+                                                      heads=heads)
+    og, lg = host(o2)[qrows], host(l2)[:, qrows]
+    for h in heads:
+        sl = slice(128 * h, 128 * h + 128)
+        err = np.abs(og[:, sl] - want[:, sl])
+        rel = np.linalg.norm(og[:, sl] - want[:, sl]) / np.linalg.norm(want[:, sl])
+        assert err.max() <= 2e-2 and rel <= 5e-3, ("staged", h, err.max(), rel)
+        assert np.max(np.abs(lg[h] - lse_want[h])) <= 2e-3

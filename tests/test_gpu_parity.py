@@ -129,7 +129,26 @@ def adversarial_rows():
     rows.append(r)
     scales = rng.uniform(0.001, 20, size=(993, 1)).astype(np.float32)
     rows.append((rng.standard_normal((993, 128)) * scales).astype(np.float32))
+    rows.append(int8_double_rounding_rows(rng))
     return np.concatenate(rows)
+
+
+def int8_double_rounding_rows(rng, n=16):
+    """Rows whose every group maximum a makes the INT8 scale rule's two roundings matter:
+    rounding a * fp32((1 + 2^-7) / 127) to fp32 and then to fp16 gives another fp16 value
+    than rounding the exact product to fp16 once.  A kernel that fuses the product and
+    the conversion into one rounding fails G1 on these groups."""
+    c8 = oracle.INT8_SCALE_FACTOR
+    found = []
+    while len(found) < 4 * n:
+        a = rng.uniform(0.5, 200.0, size=200000).astype(np.float32)
+        twice = (a * c8).astype(np.float32).astype(np.float16)
+        once = (a.astype(np.float64) * np.float64(c8)).astype(np.float16)   # exact product
+        found.extend(a[twice != once].tolist())
+    a = np.array(found[:4 * n], np.float32).reshape(n, 4)
+    r = (rng.uniform(-1.0, 1.0, size=(n, 4, 32)) * a[..., None]).astype(np.float32)
+    r[:, :, 5] = a                                  # the group maximum, exactly a
+    return r.reshape(n, 128)
 
 
 @pytest.mark.parametrize("fmt", [INT4, INT8])
