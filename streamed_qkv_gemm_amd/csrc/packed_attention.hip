@@ -192,7 +192,6 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
   // exact tier: each wave's fp6 query remainder, [chunk][lane][6 dwords]
   __shared__ __attribute__((aligned(16))) uint32_t sQ6[kFp8QK ? 1 : kWaves][kFp8QK ? 2 : 2 * 64 * 6];
   __shared__ uint32_t sKe[2][kBKV];   // the four E8M0 exponents of each key (byte g = group g)
-  __shared__ int32_t sKfmt[2];        // format of the K tile in each stage
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -557,7 +556,6 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
             *reinterpret_cast<u32x4*>(lrow + 8 * i) = v;
           }
         }
-        if (tid == 0) sKfmt[stage] = fmt;
       }
     }
   };
@@ -590,37 +588,72 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
   // into the other LDS stage and start loading the one after.)
   const bool lead = wave < kWaves / 2;
 
-  auto do_qk = [&](int stage, f32x16 (&s)[kKB]) {
+  auto do_qk = [&](int stage, int kfmt, f32x16 (&s)[kKB]) {
     const _Float16* K = sK[stage];
-    // remainder term: per 32-key block and 64-dim chunk one block-scaled fp6 MFMA; lane
-    // (key, hsel) supplies group 2 c + hsel of its key and that group's exponent
+    // Software pipeline over LDS: reads are issued in groups, each group one group of
+    // MFMAs ahead of its use, with scheduling fences between the groups so that the
+    // compiler cannot sink a read next to its MFMA (which would expose the LDS latency
+    // at every MFMA).  Order: the fp6 remainder MFMAs (chunk c = 0, then 1), then the
+    // 16 f16 MFMAs of the high part in groups of four.
+    // fp6 remainder: lane (key, hsel) supplies group 2 c + hsel of its key and that
+    // group's exponent; the query side comes from this wave's LDS copy
+    auto k6_read = [&](int kb, int c) -> i32x8 {
+      const uint8_t* row = sK6[stage] + (32 * kb + l32) * kK6Stride + 24 * hsel + 48 * c;
+      const u32x2 a0 = *reinterpret_cast<const u32x2*>(row);
+      const u32x2 a1 = *reinterpret_cast<const u32x2*>(row + 8);
+      const u32x2 a2 = *reinterpret_cast<const u32x2*>(row + 16);
+      return i32x8{(int)a0[0], (int)a0[1], (int)a1[0], (int)a1[1], (int)a2[0], (int)a2[1], 0, 0};
+    };
+    auto q6_read = [&](int c) -> i32x8 {
+      const u32x2* q6 = reinterpret_cast<const u32x2*>(&sQ6[kFp8QK ? 0 : wave][(c * 64 + lane) * 6]);
+      const u32x2 b0 = q6[0], b1 = q6[1], b2 = q6[2];
+      return i32x8{(int)b0[0], (int)b0[1], (int)b1[0], (int)b1[1], (int)b2[0], (int)b2[1], 0, 0};
+    };
+    auto kf_read = [&](int i) -> f16x8 {   // fragment i: k-step i / 2, key block i % 2
+      return *reinterpret_cast<const f16x8*>(K + (32 * (i & 1) + l32) * kKStride + 16 * (i >> 1) + 8 * hsel);
+    };
+    uint32_t ew[kKB];
+    i32x8 A[kKB], B;
+    f16x8 kf[16];
+    // group: chunk-0 fp6 operands and the first four K fragments
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) {
-      const uint32_t ew = sKe[stage][32 * kb + l32];
-      const uint8_t* row = sK6[stage] + (32 * kb + l32) * kK6Stride + 24 * hsel;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const u32x2 a0 = *reinterpret_cast<const u32x2*>(row + 48 * c);
-        const u32x2 a1 = *reinterpret_cast<const u32x2*>(row + 48 * c + 8);
-        const u32x2 a2 = *reinterpret_cast<const u32x2*>(row + 48 * c + 16);
-        const i32x8 A = {(int)a0[0], (int)a0[1], (int)a1[0], (int)a1[1], (int)a2[0], (int)a2[1], 0, 0};
-        const u32x2* q6 = reinterpret_cast<const u32x2*>(&sQ6[kFp8QK ? 0 : wave][(c * 64 + lane) * 6]);
-        const u32x2 b0 = q6[0], b1 = q6[1], b2 = q6[2];
-        const i32x8 B = {(int)b0[0], (int)b0[1], (int)b1[0], (int)b1[1], (int)b2[0], (int)b2[1], 0, 0};
-        const int ea = (int)((ew >> (8 * (2 * c + hsel))) & 0xffu);
-        const f32x16 acc = c == 0 ? f32x16{} : s[kb];
-        s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc, 2, 2, 0, ea, 0, (int)q8e[c]);
-      }
+      ew[kb] = sKe[stage][32 * kb + l32];
+      A[kb] = k6_read(kb, 0);
     }
+    B = q6_read(0);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int i = 0; i < 4; ++i) kf[i] = kf_read(i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kb = 0; kb < kKB; ++kb) {
-        const f16x8 kf = *reinterpret_cast<const f16x8*>(K + (32 * kb + l32) * kKStride + 16 * ks + 8 * hsel);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], s[kb], 0, 0, 0);
+    for (int kb = 0; kb < kKB; ++kb)
+      s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[kb], B, f32x16{}, 2, 2, 0,
+                                                               (int)((ew[kb] >> (8 * hsel)) & 0xffu), 0, (int)q8e[0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) A[kb] = k6_read(kb, 1);
+    B = q6_read(1);
+#pragma unroll
+    for (int i = 4; i < 8; ++i) kf[i] = kf_read(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+      s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[kb], B, s[kb], 2, 2, 0,
+                                                               (int)((ew[kb] >> (8 * (2 + hsel))) & 0xffu), 0, (int)q8e[1]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (g + 2 < 4) {
+#pragma unroll
+        for (int i = 4 * (g + 2); i < 4 * (g + 3); ++i) kf[i] = kf_read(i);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 4 * g; i < 4 * g + 4; ++i)
+        s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[i], qf[i >> 1], s[i & 1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (__builtin_amdgcn_readfirstlane(sKfmt[stage]) == FMT_INT8) {
+    if (kfmt == FMT_INT8) {
       const _Float16* Kl = sKlo[stage];
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
@@ -657,13 +690,15 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
 
   auto do_softmax = [&](int64_t key0, f32x16 (&s)[kKB], f16x8 (&pf)[2 * kKB]) {
     if (key0 + kBKV > p.kv_end) {
+      // keys past the end of the range: element e of block kb is key
+      // key0 + 32 kb + 8 (e >> 2) + 4 hsel + (e & 3); compare its offset within the tile
+      // (a literal) with one per-lane limit
+      const int lim = (int)(p.kv_end - key0) - 4 * hsel;
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t key = key0 + 32 * kb + 8 * (e >> 2) + 4 * hsel + (e & 3);
-          if (key >= p.kv_end) s[kb][e] = -INFINITY;
-        }
+        for (int e = 0; e < 16; ++e)
+          if (32 * kb + 8 * (e >> 2) + (e & 3) >= lim) s[kb][e] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -709,15 +744,27 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
     const int vd = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     const _Float16* vb0 = V + vk * kVStride + vcol(vk, vd);
     const _Float16* vb1 = V + (vk + 8) * kVStride + vcol(vk + 8, vd);
+    // software pipeline as in the QK step: the V^T fragments of MFMA group g + 1 (four
+    // MFMAs, one k-step of 16 keys) are read before the MFMAs of group g
+    auto vf_read = [&](int ks, int db) -> f16x8 {
+      const f16x4 lo = tr_read_f16x4(vb0 + 16 * ks * kVStride + 32 * db);
+      const f16x4 hi = tr_read_f16x4(vb1 + 16 * ks * kVStride + 32 * db);
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    f16x8 vf[2 * kKB][4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) vf[0][db] = vf_read(0, db);
 #pragma unroll
     for (int ks = 0; ks < 2 * kKB; ++ks) {
+      if (ks + 1 < 2 * kKB) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const f16x4 lo = tr_read_f16x4(vb0 + 16 * ks * kVStride + 32 * db);
-        const f16x4 hi = tr_read_f16x4(vb1 + 16 * ks * kVStride + 32 * db);
-        const f16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[ks], oacc[db], 0, 0, 0);
+        for (int db = 0; db < 4; ++db) vf[ks + 1][db] = vf_read(ks + 1, db);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[ks][db], pf[ks], oacc[db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -726,16 +773,26 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
     if (it + 2 < n_tiles) load_tile(kv0 + (int64_t)(it + 2) * kBKV, regs);
   };
 
+  // format of the K tile being multiplied, followed in scalar registers (tiles never
+  // straddle two segments: boundaries and kv_begin are multiples of 128)
+  int qk_seg = -1;
+  int64_t qk_se = 0;
+  int qk_fmt = FMT_INT4;
   for (int it = 0; it < n_tiles; ++it) {
     const int stage = it & 1;
     const int64_t key0 = kv0 + (int64_t)it * kBKV;
+    while (key0 >= qk_se) {
+      ++qk_seg;
+      qk_se = p.seg.end[qk_seg];
+      qk_fmt = head_format(p.seg, qk_seg, head);
+    }
     if (!lead) do_dq(it);
     f32x16 s[kKB];
     f16x8 pf[2 * kKB];
     if constexpr (kFp8QK)
       do_qk8(stage, s);
     else
-      do_qk(stage, s);
+      do_qk(stage, qk_fmt, s);
     do_softmax(key0, s, pf);
     do_pv(stage, pf);
     if (lead) do_dq(it);
