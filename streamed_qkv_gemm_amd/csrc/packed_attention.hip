@@ -55,11 +55,12 @@ constexpr int kKB = kBKV / 32;        // 32-key MFMA blocks per tile
 constexpr int kKStride = 128 + 8;     // f16 per K row in LDS (272 B)
 constexpr int kKTile = kBKV * kKStride;
 // V rows: 160 f16 per key (80 dwords: consecutive keys start 16 banks apart), and dim
-// bits 3-4 XORed with bits 2-3 of the key, so that the decode's 16-byte row writes and
-// the transposing 8-byte reads (8 keys x 16 dims per instruction) spread over all banks.
+// bits 3-4 XORed with bits 0-1 of the key, so that the decode's 16-byte row writes (4
+// keys x 4 groups per 16-lane phase) and the transposing 8-byte reads (8 keys x 16
+// dims per instruction) each fall in distinct banks of the 64-bank LDS.
 constexpr int kVStride = kHeadDim + 32;
 constexpr int kVTile = kBKV * kVStride;
-__device__ __forceinline__ int vcol(int k, int d) { return d ^ (((k >> 2) & 3) << 3); }
+__device__ __forceinline__ int vcol(int k, int d) { return d ^ ((k & 3) << 3); }
 constexpr float kRescaleLog2 = 8.0f;  // move the running max only past this growth
 
 
@@ -178,9 +179,10 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 // the query bytes held in registers (see the QK^T step)
 constexpr int kK8Stride = 128 + 16;
 // fp6 K rows in LDS: the four groups of one key, 24 bytes each (32 E2M3 codes in
-// dim order), then 8 bytes of padding: consecutive keys start 13 eight-byte slots
-// apart, so the 32 keys of one 8-byte operand read fall in distinct bank pairs.
-constexpr int kK6Stride = 104;
+// dim order), then 24 bytes of padding: consecutive keys start 15 eight-byte slots
+// apart, so the 32 keys of one 8-byte operand read fall in distinct bank pairs and
+// the decode's writes conflict at most 2-way.
+constexpr int kK6Stride = 120;
 
 template <bool kFp8QK>
 __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const AttnParams p) {
@@ -302,7 +304,13 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
         }
     }
     if constexpr (!kFp8QK) {
+      // the exact tier splits the query prescaled by softmax scale * log2(e), so its
+      // scores come out of the MFMAs in the base-2 units of the softmax
       f16x8 ql[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[ks][j] *= p.scale_log2;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
@@ -567,6 +575,11 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[a][e] = 0.0f;
   float m_run = -INFINITY;  // reference max of scale*log2e*score for this query column
+  // exact tier: the score accumulators start at -m_ref (the reference max, 0 before the
+  // first tile), so they come out as scale*log2e*score - m_ref and P = exp2(S) needs no
+  // per-score arithmetic; a rescale moves m_ref with the running max
+  float m_ref = 0.0f;
+  f32x16 negm = {};
   float l_run = 0.0f;       // lane-partial sum of the f16 P values
   const float c = p.scale_log2;
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
@@ -627,7 +640,7 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
-      s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[kb], B, f32x16{}, 2, 2, 0,
+      s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[kb], B, negm, 2, 2, 0,
                                                                (int)((ew[kb] >> (8 * hsel)) & 0xffu), 0, (int)q8e[0]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -707,7 +720,9 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      // the tile's largest scale*log2e*score (the exact tier's scores carry -m_ref)
+      mx = kFp8QK ? mx * c : mx + m_ref;
     }
     if (__any(mx > m_run + kRescaleLog2)) {  // wave-uniform: move every column's max
       const float m_new = fmaxf(m_run, mx);
@@ -718,13 +733,23 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+      if constexpr (!kFp8QK) {
+        const float delta = m_new - m_ref;
+        m_ref = m_new;
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s[kb][e] -= delta;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) negm[e] = -m_new;
+      }
     }
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(s[kb][e] * c - m_run);
-        const float p1 = __builtin_amdgcn_exp2f(s[kb][e + 1] * c - m_run);
+        const float p0 = __builtin_amdgcn_exp2f(kFp8QK ? s[kb][e] * c - m_run : s[kb][e]);
+        const float p1 = __builtin_amdgcn_exp2f(kFp8QK ? s[kb][e + 1] * c - m_run : s[kb][e + 1]);
         const f16x2 h2 = {(_Float16)p0, (_Float16)p1};
         l_run = __builtin_amdgcn_fdot2(h2, ones, l_run, false);
         pf[2 * kb + (e >> 3)][e & 7] = h2[0];
@@ -732,33 +757,39 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
       }
   };
 
-  auto do_pv = [&](int stage, const f16x8 (&pf)[2 * kKB]) {
-    const _Float16* V = sV[stage];
+  // P.V: O^T += V^T P^T.  The V^T fragments of the first k-step are read by pv_begin
+  // (called before the softmax, so their LDS latency hides behind it), the rest inside
+  // do_pv, one k-step ahead of their MFMAs.
+  const int pv_vk = 4 * hsel + ((lane & 15) >> 2);
+  const int pv_vd = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  auto vf_read = [&](int stage, int ks, int db) -> f16x8 {
     // A operand (V^T) by transposing LDS reads: lane L gets dim 32 db + L % 32 of keys
     // 16 ks + 4 hsel + 0..3 and 16 ks + 8 + 4 hsel + 0..3 (the MFMA's k slots 8 hsel + e
     // with bits 2 and 3 swapped, matching the key order of the P operand).  Each 16-lane
     // group reads 4 keys x 16 dims: lane c points at key (c / 4), dims 4 (c % 4) .. + 3.
-    // key k = 16 ks + 8 half + vk (vk = 4 hsel + (lane % 16) / 4), so bits 2-3 of k are
-    // (2 half + hsel) % 4 for every ks: one base per half, ks and db as offsets
-    const int vk = 4 * hsel + ((lane & 15) >> 2);
-    const int vd = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const _Float16* vb0 = V + vk * kVStride + vcol(vk, vd);
-    const _Float16* vb1 = V + (vk + 8) * kVStride + vcol(vk + 8, vd);
-    // software pipeline as in the QK step: the V^T fragments of MFMA group g + 1 (four
-    // MFMAs, one k-step of 16 keys) are read before the MFMAs of group g
-    auto vf_read = [&](int ks, int db) -> f16x8 {
-      const f16x4 lo = tr_read_f16x4(vb0 + 16 * ks * kVStride + 32 * db);
-      const f16x4 hi = tr_read_f16x4(vb1 + 16 * ks * kVStride + 32 * db);
-      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
+    // key k = 16 ks + 8 half + vk (vk = 4 hsel + (lane % 16) / 4), so bits 0-1 of k (the
+    // column swizzle) are those of vk for every ks and half: one base per half, ks and
+    // db as offsets
+    const _Float16* V = sV[stage];
+    const _Float16* vb0 = V + pv_vk * kVStride + vcol(pv_vk, pv_vd);
+    const _Float16* vb1 = V + (pv_vk + 8) * kVStride + vcol(pv_vk + 8, pv_vd);
+    const f16x4 lo = tr_read_f16x4(vb0 + 16 * ks * kVStride + 32 * db);
+    const f16x4 hi = tr_read_f16x4(vb1 + 16 * ks * kVStride + 32 * db);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto pv_begin = [&](int stage, f16x8 (&vf0)[4]) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) vf0[db] = vf_read(stage, 0, db);
+  };
+  auto do_pv = [&](int stage, const f16x8 (&pf)[2 * kKB], const f16x8 (&vf0)[4]) {
     f16x8 vf[2 * kKB][4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) vf[0][db] = vf_read(0, db);
+    for (int db = 0; db < 4; ++db) vf[0][db] = vf0[db];
 #pragma unroll
     for (int ks = 0; ks < 2 * kKB; ++ks) {
       if (ks + 1 < 2 * kKB) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) vf[ks + 1][db] = vf_read(ks + 1, db);
+        for (int db = 0; db < 4; ++db) vf[ks + 1][db] = vf_read(stage, ks + 1, db);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -793,8 +824,10 @@ __global__ __launch_bounds__(kThreads, 1) void packed_attention_kernel(const Att
       do_qk8(stage, s);
     else
       do_qk(stage, qk_fmt, s);
+    f16x8 vf0[4];
+    pv_begin(stage, vf0);
     do_softmax(key0, s, pf);
-    do_pv(stage, pf);
+    do_pv(stage, pf, vf0);
     if (lead) do_dq(it);
     __syncthreads();
   }

@@ -298,11 +298,16 @@ def test_accumulate_two_halves_equals_full(lib):
     o, l = lib.packed_kv_attention(store, kv_end=512)
     lib.packed_kv_attention(store, kv_begin=512, accumulate=True, o=o, lse=l)
     torch.cuda.synchronize()
-    assert torch.allclose(o, o_full, rtol=0, atol=2e-3)
+    # the two launches round P to f16 against other reference maxima than the single
+    # pass: each P carries a relative error up to 2^-12 either way, so O may move by up
+    # to 2 * 2^-12 * max |V| (|V| <= 10 here) = 4.9e-3 between the two; both are gated
+    # against the oracle below
+    assert torch.allclose(o, o_full, rtol=0, atol=5e-3)
     assert torch.allclose(l, l_full, rtol=0, atol=1e-3)
     rows = np.arange(0, N, 7)
     o_ref, lse_ref = oracle_attention(store, layout, H, rows)
     attention_gate(host(o)[rows], o_ref, "accumulated O")
+    attention_gate(host(o_full)[rows], o_ref, "single-pass O")
 
 
 def test_query_and_key_subranges(lib):
