@@ -36,7 +36,7 @@ extern "C" {
 #define SQG_API
 #endif
 
-#define SQG_VERSION 131          /* 1.3.1 */
+#define SQG_VERSION 140          /* 1.4.0 */
 #define SQG_HEAD_DIM 128
 #define SQG_GROUP 32
 #define SQG_MAX_SEGMENTS 16
@@ -46,6 +46,7 @@ typedef enum sqg_status {
   SQG_ERR_INVALID_ARGUMENT = -1,   /* null pointer, bad size, bad range policy ... */
   SQG_ERR_UNSUPPORTED = -2,        /* shape outside what the kernels implement */
   SQG_ERR_MISALIGNED = -3,         /* pointer not 16-byte aligned or stride not a multiple of 8 */
+  SQG_ERR_WORKSPACE_TOO_SMALL = -4,/* a workspace (or the device scratch) cannot hold what the call needs */
   SQG_ERR_HIP = -5                 /* a HIP launch reported an error */
 } sqg_status;
 
@@ -331,6 +332,26 @@ SQG_API int64_t sqg_qrecompute_workspace_bytes(int64_t n_query_rows, int64_t q_c
  * plus one chunk of Q.  Results equal sqg_streamed_qkv_quant (SQG_EMIT_Q) followed by
  * sqg_packed_kv_attention bit for bit. */
 SQG_API int sqg_packed_kv_attention_qrecompute(const sqg_qrecompute_args* args, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): sqg_packed_kv_attention_qrecompute
+ * with the one-chunk Q workspace taken from a fixed device scratch of
+ * sqg_noalloc_scratch_bytes() bytes (64 MiB) that the library holds on every GPU it runs
+ * on until the process ends.  args->workspace must be NULL and args->workspace_bytes 0.
+ * With q_chunk_rows 0 the chunk is the default one shrunk to the largest multiple of 256
+ * rows whose chunks (a folded tail of up to 511 rows included) fit the scratch: 4096 rows at
+ * d_model 7168.  An explicit q_chunk_rows whose chunks do not fit, or a d_model for which
+ * 256 rows do not, returns SQG_ERR_WORKSPACE_TOO_SMALL.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine); the scratch's
+ * device address is looked up once per device (hipGetSymbolAddress) on the first call
+ * with that device current.  Every call on one GPU shares that GPU's scratch, which keeps
+ * the last call's contents (each chunk's Q is written before it is read, so nothing needs
+ * clearing): calls that overlap in time on one GPU (other streams, other threads) race
+ * and must not be issued.  Results equal sqg_packed_kv_attention_qrecompute bit for bit. */
+SQG_API int sqg_packed_kv_attention_qrecompute_noalloc(const sqg_qrecompute_args* args, void* stream);
+
+/* Bytes of the device scratch sqg_packed_kv_attention_qrecompute_noalloc uses. */
+SQG_API int64_t sqg_noalloc_scratch_bytes(void);
 
 /* sqg_streamed_qkv_quant with the packed K/V kept in host memory: for each key block,
  * the kernel writes the block's K/V into a device staging block store (alternating

@@ -123,6 +123,8 @@ def load(path: Optional[str] = None):
     lib.sqg_qrecompute_workspace_bytes.restype = _c_i64
     lib.sqg_qrecompute_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i32]
     lib.sqg_packed_kv_attention_qrecompute.argtypes = [ctypes.POINTER(QRecomputeArgs), _vp]
+    lib.sqg_packed_kv_attention_qrecompute_noalloc.argtypes = [ctypes.POINTER(QRecomputeArgs), _vp]
+    lib.sqg_noalloc_scratch_bytes.restype = _c_i64
     lib.sqg_test_quant_pack_f32.argtypes = [_vp, _c_i64, _c_i32, _vp, _vp, _vp]
     lib.sqg_test_fwht_f32.argtypes = [_vp, _vp, _c_i64, _c_i32, _vp]
     for name, cls in ((0, Range), (1, Layout), (2, QkvArgs), (3, AttnArgs), (4, QRecomputeArgs),
@@ -375,6 +377,45 @@ def packed_kv_attention_qrecompute(store: Dict, x: torch.Tensor, w_qkv: torch.Te
     r.workspace = _dev_ptr(workspace, "workspace")
     r.workspace_bytes = workspace.numel() * workspace.element_size()
     _check(lib.sqg_packed_kv_attention_qrecompute(ctypes.byref(r), _stream(x.device)))
+    return o, lse
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the device scratch the allocation-free Q-recompute entry point uses."""
+    return load().sqg_noalloc_scratch_bytes()
+
+
+def packed_kv_attention_qrecompute_noalloc(store: Dict, x: torch.Tensor, w_qkv: torch.Tensor,
+                                           o: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                                           q_norm_w: Optional[torch.Tensor] = None,
+                                           rope_cos: Optional[torch.Tensor] = None,
+                                           rope_sin: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                                           q_chunk_rows: int = 0, q_begin: int = 0, q_end: int = 0,
+                                           kv_begin: int = 0, kv_end: int = 0, kv_block: int = 0,
+                                           accumulate: bool = False, softmax_scale: float = 0.0,
+                                           qk_mode: int = SQG_QK_EXACT):
+    """packed_kv_attention_qrecompute whose Q workspace is the library's own device scratch:
+    the call allocates nothing, so the caller passes the outputs (o, and lse when the call
+    merges: accumulate or kv_block > 0).  Calls overlapping on one GPU race on the scratch."""
+    lib = load()
+    N, d = x.shape
+    for t, nm in ((x, "x"), (w_qkv, "w_qkv")):
+        if t.dtype != torch.bfloat16 or t.stride(-1) != 1:
+            raise ValueError("%s must be a row-major bf16 tensor" % nm)
+    if o is None or (lse is None and (accumulate or kv_block > 0)):
+        raise ValueError("the allocation-free entry point takes its outputs from the caller (o, and "
+                         "lse when the call merges: accumulate or kv_block > 0)")
+    a, _keep, o, lse = _attn_args(store, N, d, x.device, q_begin, q_end, kv_begin, kv_end, kv_block,
+                                  accumulate, o, lse, o.dtype, softmax_scale, False, qk_mode)
+    r = QRecomputeArgs()
+    r.attn = a
+    r.x, r.ldx = _dev_ptr(x, "x"), x.stride(0)
+    r.w_qkv, r.ldw = _dev_ptr(w_qkv, "w_qkv"), w_qkv.stride(0)
+    r.q_norm_w = _dev_ptr(q_norm_w, "q_norm_w")
+    r.rope_cos, r.rope_sin = _dev_ptr(rope_cos, "rope_cos"), _dev_ptr(rope_sin, "rope_sin")
+    r.eps, r.reserved, r.q_chunk_rows = eps, 0, q_chunk_rows
+    r.workspace, r.workspace_bytes = None, 0
+    _check(lib.sqg_packed_kv_attention_qrecompute_noalloc(ctypes.byref(r), _stream(x.device)))
     return o, lse
 
 

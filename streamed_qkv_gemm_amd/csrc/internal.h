@@ -79,6 +79,12 @@ int launch_test_quant_pack(const float* r, int64_t rows, int32_t fmt, void* code
 int launch_test_fwht(const float* in, float* out, int64_t rows, int32_t normalize, void* stream);
 const char* hip_error_text(int err);
 
+// Device scratch of the allocation-free Q-recompute entry point: kScratchBytes on every
+// device, shared by all calls on that device.  scratch_for_current_device returns its
+// address on the calling thread's current device (a hipError_t value, 0 on success).
+constexpr int64_t kScratchBytes = 64ll << 20;
+int scratch_for_current_device(void** ptr);
+
 // Asynchronous copy on `stream` (hipMemcpyAsync); returns a hipError_t value.
 enum CopyKind { kHostToDevice = 1, kDeviceToHost = 2 };
 int copy_async(void* dst, const void* src, int64_t bytes, CopyKind kind, void* stream);

@@ -463,6 +463,7 @@ SQG_API const char* sqg_status_string(int status) {
     case SQG_ERR_INVALID_ARGUMENT: return "invalid argument";
     case SQG_ERR_UNSUPPORTED: return "unsupported shape";
     case SQG_ERR_MISALIGNED: return "misaligned pointer or stride";
+    case SQG_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case SQG_ERR_HIP: return "HIP error";
     default: return "unknown status";
   }
@@ -608,8 +609,12 @@ SQG_API int64_t sqg_qrecompute_workspace_bytes(int64_t n_query_rows, int64_t q_c
   return rows * d_model * 2;
 }
 
-SQG_API int sqg_packed_kv_attention_qrecompute(const sqg_qrecompute_args* a, void* stream) {
-  if (!a) return fail(SQG_ERR_INVALID_ARGUMENT, "args is NULL");
+namespace {
+
+// Q-recompute attention with the given Q workspace (the caller's, or the device scratch
+// of the allocation-free entry); `scratch` chooses which the argument checks describe.
+int qrecompute_run(const sqg_qrecompute_args* a, void* workspace, int64_t workspace_bytes,
+                   bool scratch, void* stream) {
   const sqg_attn_args& at = a->attn;
   sqg::AttnParams ap;
   int64_t kv_end = 0;
@@ -627,30 +632,53 @@ SQG_API int sqg_packed_kv_attention_qrecompute(const sqg_qrecompute_args* a, voi
     return fail(SQG_ERR_INVALID_ARGUMENT, "rope_cos and rope_sin must both be set or both be NULL");
   if (a->q_norm_w && !(a->eps >= 0.0f && std::isfinite(a->eps)))
     return fail(SQG_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if (scratch && (a->workspace || a->workspace_bytes))
+    return fail(SQG_ERR_INVALID_ARGUMENT,
+                "the allocation-free entry uses its own device scratch: workspace must be NULL and "
+                "workspace_bytes 0");
+  // chunk rows: the caller's, else the default; the scratch entry shrinks the default to
+  // the largest multiple of 256 rows whose chunks fit its scratch (a last chunk may run
+  // up to 511 rows longer, the folded tail)
+  int64_t size = a->q_chunk_rows == 0 ? default_q_chunk(at.n_heads) : a->q_chunk_rows;
+  if (scratch && a->q_chunk_rows == 0) {
+    const int64_t fit_rows = workspace_bytes / (2 * d);
+    const int64_t fit = fit_rows > 511 ? (fit_rows - 511) / 256 * 256 : 0;
+    if (fit < size) size = fit;
+    if (size <= 0)
+      return fail(SQG_ERR_WORKSPACE_TOO_SMALL,
+                  "chunks of 256 query rows (and a folded tail) of d_model %lld need %lld bytes, more "
+                  "than the %lld-byte device scratch",
+                  (long long)d, (long long)(767 * 2 * d), (long long)workspace_bytes);
+  }
   if (empty) return ok();
   const int64_t n_q = ap.q_end - ap.q_begin;
-  const int64_t need = sqg_qrecompute_workspace_bytes(n_q, a->q_chunk_rows, at.d_model);
-  if (!a->x || !a->w_qkv || !a->workspace)
+  const int64_t need = sqg_qrecompute_workspace_bytes(n_q, size, at.d_model);
+  if (!a->x || !a->w_qkv || (!scratch && !workspace))
     return fail(SQG_ERR_INVALID_ARGUMENT, "a required device pointer is NULL");
-  if (a->workspace_bytes < need)
-    return fail(SQG_ERR_INVALID_ARGUMENT, "workspace holds %lld bytes, %lld needed",
-                (long long)a->workspace_bytes, (long long)need);
+  if (workspace_bytes < need)
+    return fail(SQG_ERR_WORKSPACE_TOO_SMALL, "%s holds %lld bytes, %lld needed for chunks of %lld rows",
+                scratch ? "the device scratch" : "workspace", (long long)workspace_bytes,
+                (long long)need, (long long)size);
   if (a->ldx < d || a->ldw < 3 * d)
     return fail(SQG_ERR_INVALID_ARGUMENT, "row strides must be >= the row length (ldx %lld, ldw %lld)",
                 (long long)a->ldx, (long long)a->ldw);
   if (a->ldx % 8 || a->ldw % 8) return fail(SQG_ERR_MISALIGNED, "row strides must be multiples of 8 elements");
   if (d * a->ldw * 2 > 0x7fffffffLL || 256 * a->ldx * 2 > 0x7fffffffLL)
     return fail(SQG_ERR_UNSUPPORTED, "W (or a 256-row slice of x) exceeds the 2 GiB a buffer resource addresses");
-  const void* ptrs[] = {a->x, a->w_qkv, a->workspace, a->q_norm_w, a->rope_cos, a->rope_sin};
+  const void* ptrs[] = {a->x, a->w_qkv, workspace, a->q_norm_w, a->rope_cos, a->rope_sin};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return fail(SQG_ERR_MISALIGNED, "device pointer %p is not 16-byte aligned", ptr);
+  if (scratch) {   // every argument is valid: the scratch's address on this device
+    st = launch_status(sqg::scratch_for_current_device(&workspace), "device scratch lookup");
+    if (st != SQG_OK) return st;
+  }
 
   // Q-only projection of one chunk into the workspace (row t at row t - chunk start)
   sqg::QkvParams qp;
   std::memset(&qp, 0, sizeof qp);
   qp.x = static_cast<const uint16_t*>(a->x);
   qp.w = static_cast<const uint16_t*>(a->w_qkv);
-  qp.q = static_cast<uint16_t*>(a->workspace);
+  qp.q = static_cast<uint16_t*>(workspace);
   qp.q_norm_w = a->q_norm_w;
   qp.rope_cos = a->rope_cos;
   qp.rope_sin = a->rope_sin;
@@ -667,9 +695,8 @@ SQG_API int sqg_packed_kv_attention_qrecompute(const sqg_qrecompute_args* a, voi
   qp.n_col_tiles = (int32_t)(d / 256);
   qp.seg = ap.seg;
 
-  ap.q = static_cast<const uint16_t*>(a->workspace);
+  ap.q = static_cast<const uint16_t*>(workspace);
   ap.ldq = d;
-  const int64_t size = a->q_chunk_rows == 0 ? default_q_chunk(at.n_heads) : a->q_chunk_rows;
   for (const auto& c : chunk_plan(n_q, size, 512)) {
     const int64_t c0 = ap.q_begin + c.first;  // chunk offsets are relative to the range start
     const int64_t c1 = ap.q_begin + c.second;
@@ -687,6 +714,20 @@ SQG_API int sqg_packed_kv_attention_qrecompute(const sqg_qrecompute_args* a, voi
   }
   return ok();
 }
+
+}  // namespace
+
+SQG_API int sqg_packed_kv_attention_qrecompute(const sqg_qrecompute_args* a, void* stream) {
+  if (!a) return fail(SQG_ERR_INVALID_ARGUMENT, "args is NULL");
+  return qrecompute_run(a, a->workspace, a->workspace_bytes, false, stream);
+}
+
+SQG_API int sqg_packed_kv_attention_qrecompute_noalloc(const sqg_qrecompute_args* a, void* stream) {
+  if (!a) return fail(SQG_ERR_INVALID_ARGUMENT, "args is NULL");
+  return qrecompute_run(a, nullptr, sqg::kScratchBytes, true, stream);
+}
+
+SQG_API int64_t sqg_noalloc_scratch_bytes(void) { return sqg::kScratchBytes; }
 
 SQG_API int sqg_streamed_qkv_quant_staged(const sqg_qkv_args* a, const sqg_staged_kv* sk,
                                           void* stream) {

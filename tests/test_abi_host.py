@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 10
     for n in names:
         assert hasattr(lib, n), n
-    assert sqg.version() == 131
+    assert sqg.version() == 140
 
 
 def test_struct_sizes_match_binding():
@@ -200,8 +200,8 @@ def qrec_args(**kw):
 
 
 @pytest.mark.parametrize("kw,status,msg", [
-    (dict(workspace_bytes=1024 * 512 * 2 - 2), -1, b"workspace"),
-    (dict(q_chunk_rows=256, workspace_bytes=256 * 512 * 2 - 2), -1, b"workspace"),
+    (dict(workspace_bytes=1024 * 512 * 2 - 2), -4, b"workspace"),
+    (dict(q_chunk_rows=256, workspace_bytes=256 * 512 * 2 - 2), -4, b"workspace"),
     (dict(workspace=None), -1, b"NULL"),
     (dict(x=None), -1, b"NULL"),
     (dict(reserved=1), -1, b"reserved"),
@@ -416,3 +416,23 @@ def test_staged_entry_specific_errors():
     # empty query range: nothing to do
     b = attn_args(q_begin=5, q_end=5)
     assert lib.sqg_packed_kv_attention_staged(ctypes.byref(b), ctypes.byref(s), None) == 0
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(workspace=FAKE), -1, b"workspace must be NULL"),
+    (dict(workspace=None, workspace_bytes=4096), -1, b"workspace must be NULL"),
+    # explicit chunks of 65536 rows of d 512 need 64 MiB + the folded tail: beyond the scratch
+    (dict(workspace=None, workspace_bytes=0, q_chunk_rows=65536, attn_n_tokens=66000), -4, b"scratch"),
+    (dict(workspace=None, workspace_bytes=0, x=None), -1, b"NULL"),
+])
+def test_noalloc_qrecompute_argument_errors(kw, status, msg):
+    # the allocation-free entry point checks its arguments like the Q-recompute entry and
+    # refuses a workspace of its own or chunks beyond its device scratch, before any launch
+    lib = sqg.load()
+    r = qrec_args(**kw)
+    assert lib.sqg_packed_kv_attention_qrecompute_noalloc(ctypes.byref(r), None) == status
+    assert msg in lib.sqg_last_error()
+
+
+def test_noalloc_scratch_size():
+    assert sqg.noalloc_scratch_bytes() == 64 << 20
