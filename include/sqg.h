@@ -67,8 +67,12 @@ typedef enum sqg_kv_format {
 typedef enum sqg_out_dtype { SQG_F32 = 0, SQG_BF16 = 1, SQG_F16 = 2 } sqg_out_dtype;
 
 /* Precision of the scores QK^T in attention.
- * SQG_QK_EXACT: the rotated query as an f16 high part plus an f16 remainder against
- *   the exactly dequantised f16 keys (two f16 MFMAs per step; the parity tier).
+ * SQG_QK_EXACT: the parity tier.  The rotated query, prescaled by softmax_scale *
+ *   log2(e), is split into an f16 high part and its remainder; the scores are the f16
+ *   MFMA of the high part against the dequantised f16 keys plus the block-scaled fp6
+ *   (E2M3, one E8M0 exponent per group of 32 dims) MFMA of the remainder against the
+ *   keys, fp32 accumulation.  INT4 and BF16 keys are exact in f16; INT8 keys add the
+ *   f16 remainder of code * scale against the high part.
  * SQG_QK_FP8: [VL] kvi8s section (an approximation tier: rotated Q and K, QK^T on
  *   low-precision matrix cores straight from the store).  The rotated query and the
  *   decoded keys are quantised per group of 32 dims to OCP E4M3 values with one E8M0
@@ -172,7 +176,8 @@ typedef struct sqg_attn_args {
   int64_t q_begin, q_end;      /* query rows [q_begin, q_end); q_end 0 = N */
   int64_t kv_begin, kv_end;    /* keys [kv_begin, kv_end); kv_end 0 = N; kv_begin % 128 == 0 */
   int64_t kv_block;            /* 0 = one pass; > 0 = key blocks of this many keys (multiple of
-                                  128, last block shorter than 512 folded) merged by log-sum-exp */
+                                  128, last block shorter than 512 folded) merged by log-sum-exp,
+                                  in one launch (see sqg_packed_kv_attention) */
   int32_t accumulate;          /* 1 = merge into the existing (O, lse) instead of overwriting */
   float softmax_scale;         /* 0 = 1/sqrt(128) */
   void* o;                     /* device, [N, ldo] of o_dtype, out (model basis) */
@@ -297,8 +302,10 @@ SQG_API int sqg_rope_table(int64_t pos0, int64_t n, double theta, float* cos_out
  *     given: split-half RoPE of q and k ([VL] helpers `_norm_rope`);
  *   - Q = bf16(q) stored in the model basis;
  *   - K and V: r = u H / sqrt(128) (Sylvester Hadamard, [VL] kvi8r `_hadamard`),
- *     per group of 32: s = fp16(max|r| / qmax), code = clamp(rne(r / s), +-qmax)
- *     (qmax 7 for INT4, 127 for INT8 ranges), packed per sqg_kv_layout.
+ *     per group of 32 with a = max|r|: INT4 s = fp16(a / 7 in fp32, rounded up to 8
+ *     significant bits), INT8 s = fp16(a * fp32((1 + 2^-7) / 127)) (round to nearest
+ *     even); code = clamp(rne(r / s), +-qmax) with qmax 7 (INT4) or 127 (INT8 ranges),
+ *     IEEE fp32 division; packed per sqg_kv_layout.
  * Chunks only partition the launches: results do not depend on chunk_rows.  `emit`
  * restricts the launch to Q or to the K/V store; what it writes is identical to the
  * same part of a full call. */
@@ -310,10 +317,15 @@ SQG_API int sqg_streamed_qkv_quant(const sqg_qkv_args* args, void* stream);
  * scores and P.V run against K/V dequantised in on-chip memory in the rotated
  * basis, blocks combine by online softmax, and the output is rotated back once.
  * Non-causal, no mask.  O = softmax(scale * Q K^T) V and lse = ln sum exp(scale * Q K^T)
- * over keys [kv_begin, kv_end).  With kv_block > 0 the keys are processed in
- * blocks whose partial (O, lse) are merged as in [VL] kvi8r `_online_combine`;
+ * over keys [kv_begin, kv_end).  kv_block > 0 names the pages' key blocks ([VL] kvi8r
+ * `_online_combine`): one launch walks every block, and continuing the running
+ * maximum, sum and output across a block boundary is the log-sum-exp merge of the
+ * blocks' partial (O, lse), so the result equals the merge of per-block passes up to
+ * fp32 rounding; kv_block is validated (multiple of 128) and requires lse.
  * accumulate = 1 merges into the (O, lse) already in the buffers (requires
- * o_dtype SQG_F32). */
+ * o_dtype SQG_F32).  Errors are reported before anything is enqueued; a store whose
+ * code bytes of one (segment, head), or whose scales of one head, exceed 2 GiB is
+ * SQG_ERR_UNSUPPORTED (the kernel's 32-bit buffer ranges). */
 SQG_API int sqg_packed_kv_attention(const sqg_attn_args* args, void* stream);
 
 /* Host only.  Bytes of the Q workspace sqg_packed_kv_attention_qrecompute needs for
@@ -370,8 +382,10 @@ SQG_API int sqg_streamed_qkv_quant_staged(const sqg_qkv_args* args, const sqg_st
  * through the log-sum-exp ([VL] kvi8r section, `_online_combine`).  The blocks take
  * the place of kv_block (args->kv_block is ignored), so with more than one block an
  * lse buffer and SQG_F32 output are required.  args->kpack, vpack, kscale, vscale are
- * ignored.  Results equal sqg_packed_kv_attention on the device store with kv_block =
- * block_rows bit for bit.  The device never holds more than two blocks of K/V. */
+ * ignored.  Results equal one sqg_packed_kv_attention call per block on the device
+ * store (keys [block begin, block end), accumulate after the first) bit for bit, and
+ * the single-launch device path with kv_block = block_rows up to fp32 rounding.  The
+ * device never holds more than two blocks of K/V. */
 SQG_API int sqg_packed_kv_attention_staged(const sqg_attn_args* args, const sqg_staged_kv* staged,
                                            void* stream);
 

@@ -35,12 +35,17 @@
 // The transposed products keep a query's scores and its 128 output values in one
 // lane pair, so the softmax statistics and the final inverse rotation are
 // register-local apart from one exchange with lane ^ 32 (v_permlane32_swap inside
-// the loop).  The query's high part stays in registers; its remainder waits in LDS
-// next to the tiles; the K and V fragment reads sit in plain loops next to their
-// MFMAs and the compiler places them ahead (explicit double-buffered prefetch and
-// scheduling fences measured 1-2% slower).  The running maximum is
-// only moved (and O rescaled) when a column's maximum grows by more than 2^8, so
-// most tiles skip the rescale; P then stays below 256, well inside f16.
+// the loop).  The query is prescaled by softmax scale * log2(e) before the split, and
+// each tile's score accumulators start at minus the running reference maximum, so the
+// MFMAs deliver the exponent of P = exp2(S) directly.  The query's f16 high part stays
+// in registers and its fp6 remainder in LDS (one copy per wave).  QK^T and P.V read
+// their LDS fragments one MFMA group ahead, with scheduling fences between the groups
+// so that the compiler cannot sink a read next to the MFMA that consumes it.  The
+// running maximum is only moved (and O rescaled) when a column's maximum grows by more
+// than 2^8, so most tiles skip the rescale; P then stays below 256, well inside f16.
+// One launch walks every key of the call: continuing (m, l, O) across a key-block
+// boundary is the log-sum-exp merge of the blocks (VRAM Lab page, kvi8r section,
+// `_online_combine`), so KV blocking costs nothing here.
 #include "device_common.h"
 #include "internal.h"
 
