@@ -29,7 +29,13 @@ DEFAULT_WORKLOAD = "h3_217k_normrope"
 # counters scaled by the same counters on a device copy of known size, keyed by the
 # kernel, the SHA-256 of the kernel source they were taken on, and the workload.  A
 # changed kernel reports null until the counters are taken again.
-MEASURED_TRAFFIC = {}
+MEASURED_TRAFFIC = {
+    # profiles/hbm_traffic_h3_217k_normrope.md
+    ("packed_attention_kernel", "a2cc8cd6ff8a4470c90c56537c46f5b6fb15d6e5ea8ff575b3631e1ac94f5c30",
+     "h3_217k_normrope"): 1.0461e+11,
+    ("qkv_quant_kernel", "f13aaa425c9eaeca854aa202c1af9fbb86ec301034ca1be3368906e93aac08bb",
+     "h3_217k_normrope"): 7.6023e+09,
+}
 
 
 def parse():
