@@ -277,6 +277,24 @@ def test_g3_attention(lib, N, d, ranges):
     assert np.max(np.abs(host(lse) - lse_ref)) <= 2e-3
 
 
+@pytest.mark.parametrize("scale", [0.02, 0.25, 1.0])
+def test_g3_softmax_scale(lib, scale):
+    # Non-default softmax scales, with and without KV blocks.  At 1.0 the scores are ~11x
+    # the default's, so the running maximum moves past the 2^8 threshold (and O is
+    # rescaled) on many tiles; at 0.02 the softmax is nearly flat.  The LSE bound grows
+    # with the scale because its error is relative to the scores.
+    N, d = 1000, 512
+    store, layout, H = attention_case(lib, N, d, [(0, 256, INT8), (256, N, INT4)], seed=91)
+    rows = np.arange(N)
+    lse_tol = 2e-3 * max(1.0, scale * 128 ** 0.5)
+    for kv_block in (0, 256):
+        o, lse = lib.packed_kv_attention(store, softmax_scale=scale, kv_block=kv_block)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle_attention(store, layout, H, rows, scale=scale, kv_block=kv_block)
+        attention_gate(host(o), o_ref, "O at scale %g, kv_block %d" % (scale, kv_block))
+        assert np.max(np.abs(host(lse) - lse_ref)) <= lse_tol, (scale, kv_block)
+
+
 def test_g3_kv_blocks_merge(lib):
     N, d = 1024, 512
     store, layout, H = attention_case(lib, N, d, None, seed=71)
